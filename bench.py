@@ -1,0 +1,202 @@
+"""Throughput of QUOKA's per-chunk hot path on one MI355X.
+
+A step is one pass of the whole path (query subselection, key scoring, top-B
+select, K/V gather, chunk attention) over one layer's chunk, all heads, with
+inputs already resident in HBM. Several rotated copies of the inputs are
+cycled through so that consecutive steps do not hit the 256 MB last-level
+cache with the previous step's history keys.
+
+Prints ONE JSON line. The roofline entry is for the dominant kernel (chunk
+attention, bf16 MFMA); its duration is measured live with HIP events around
+that single launch on the stream it runs on. cpu_baseline times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+
+usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config llama8b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (vector / MFMA)
+PEAK_HBM_GBS = 8000.0
+
+DESCR = {
+    "tiny": "1 seq, 1q/1kv heads, d=64, fp32, L=1024, C=128, Nq=16, B=128",
+    "llama8b": "Llama-3-8B-shaped layer: 1 seq, 32q/8kv heads, d=128, bf16, L=32768, C=2048, "
+               "Nq=64, B=2048",
+    "long": "long-history layer: 1 seq, 32q/8kv heads, d=128, bf16, L=131072, C=4096, Nq=128, "
+            "B=4096",
+    "narrow": "narrow-GQA layer: 1 seq, 28q/4kv heads, d=128, bf16, L=65536, C=1024, Nq=32, "
+              "B=1024",
+    "ragged": "8 ragged seqs, L=4K..96K, C=512 each, 32q/8kv heads, d=128, bf16, Nq=32, B=1024",
+}
+
+
+def attention_flops(w) -> float:
+    """Algorithmic FLOPs of the chunk attention: 4 d H_q per visible (query, key) pair,
+    pairs = sum_s C_s B_eff + C_s (C_s + 1) / 2."""
+    pairs = 0
+    for C, L in zip(w.chunk_lens, w.hist_lens):
+        pairs += C * min(w.budget, L) + C * (C + 1) // 2
+    return 4.0 * w.head_dim * w.num_q_heads * pairs
+
+
+def scorer_bytes(w) -> float:
+    """Algorithmic HBM bytes of the scorer: every history key once, plus the scores."""
+    elem = 2 if w.dtype == "bf16" else 4
+    return w.k_hist.shape[0] * w.num_kv_heads * (w.head_dim * elem + 4)
+
+
+def cpu_baseline(w, max_heads: int = 2):
+    """The fp64 oracle on KV heads 0..max_heads-1 of sequence 0 (selection and
+    attention of their query heads); scaled to the whole layer's tokens/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    heads = list(range(min(max_heads, w.num_kv_heads)))
+    t0 = time.perf_counter()
+    oracle.prefill_chunk(w.q, w.k_hist, w.v_hist, w.k_chunk, w.v_chunk, w.cu_chunk,
+                         w.cu_hist, w.num_kv_heads, w.n_q, w.budget, heads=heads)
+    dt = time.perf_counter() - t0
+    layer_s = dt * w.num_kv_heads / len(heads)
+    return {
+        "value": float(w.cu_chunk[-1]) / layer_s,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle, whole path for KV heads {heads} of {w.num_kv_heads} "
+                   f"({len(heads) * w.num_q_heads // w.num_kv_heads} query heads), "
+                   f"{dt:.1f} s, scaled by {w.num_kv_heads}/{len(heads)} to the layer; "
+                   f"host has {cores} cores, BLAS used {threads} threads"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b", choices=sorted(DESCR))
+    ap.add_argument("--input-sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is built "
+              "for a single MI355X and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_prefill_kv_amd as cpk
+    from workloads import make_config
+
+    w = make_config(args.config)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shape = cpk.Shape(w.cu_chunk, w.cu_hist, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                      w.dtype, device=dev)
+    base = {n: torch.from_numpy(getattr(w, n)).to(dt).to(dev)
+            for n in ("q", "k_hist", "v_hist", "k_chunk", "v_chunk")}
+    # rotated copies of the history (same work, different bytes) to defeat the LLC
+    sets = [base]
+    TL = w.k_hist.shape[0]
+    for r in range(1, max(1, args.input_sets)):
+        shift = (r * TL) // args.input_sets
+        sets.append(dict(base, k_hist=torch.roll(base["k_hist"], shift, 0).contiguous(),
+                         v_hist=torch.roll(base["v_hist"], shift, 0).contiguous()))
+    S, Hkv, B = w.num_seqs, w.num_kv_heads, w.budget
+    ws = cpk.alloc_workspace(shape, w.n_q, B)
+    sel = torch.empty((S, Hkv, B), dtype=torch.int32, device=dev)
+    k_sel = torch.empty((S, Hkv, B, w.head_dim), dtype=dt, device=dev)
+    v_sel = torch.empty_like(k_sel)
+    out = torch.empty_like(base["q"])
+
+    def step(i, ev=None):
+        x = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        cpk.select(shape, x["q"], x["k_hist"], w.n_q, B, sel_idx=sel, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        cpk.gather(shape, x["k_hist"], x["v_hist"], sel, B, k_sel=k_sel, v_sel=v_sel)
+        if ev is not None:
+            ev[2].record()
+        cpk.chunk_attn(shape, x["q"], k_sel, v_sel, B, x["k_chunk"], x["v_chunk"], out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    sel_us = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    gat_us = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    att_us = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+
+    tokens = float(w.cu_chunk[-1])
+    flops = attention_flops(w)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops / (att_us * 1e-6) / 1e12
+    gather_bytes = 2.0 * 2 * S * Hkv * B * w.head_dim * (2 if w.dtype == "bf16" else 4)
+    line = {
+        "metric": "chunk-prefill attn tokens/sec per layer (select+gather+attn); "
+                  "HBM/MFMA % of peak",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded generators, no dataset or weights)",
+        "config": {"workload": f"{args.config}: {DESCR[args.config]}",
+                   "chunk_tokens": int(tokens), "history_tokens": int(TL),
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "q_budget": w.n_q, "kv_budget": B,
+                   "input_sets": len(sets)},
+        "stages_us": {"select": round(sel_us, 2), "gather": round(gat_us, 2),
+                      "chunk_attn": round(att_us, 2)},
+        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel" if w.dtype == "bf16"
+                     else "attn_valu_kernel",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "algorithmic": {"flops_per_launch": flops}},
+        "secondary": {"gather_GBps": gather_bytes / (gat_us * 1e-6) / 1e9,
+                      "gather_frac_hbm": gather_bytes / (gat_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                      "scorer_bytes": scorer_bytes(w)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

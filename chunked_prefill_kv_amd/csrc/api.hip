@@ -1,0 +1,310 @@
+// C ABI of the QUOKA per-chunk hot path: argument validation, workspace
+// layout and the launch sequence on the caller's stream. Declared and
+// documented in include/quoka.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "common.h"
+#include "internal.h"
+#include "quoka.h"
+
+namespace quoka {
+namespace {
+
+thread_local char g_err[512] = "";
+
+quoka_status fail(quoka_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool sync_mode() {
+  static const bool on = [] {
+    const char* v = std::getenv("QUOKA_SYNC");
+    return v && v[0] && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+quoka_status hip_check(hipError_t e, const char* what, hipStream_t st) {
+  if (e == hipSuccess && sync_mode()) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(QUOKA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return QUOKA_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest dynamic LDS the scorer asks for; raised once per device.
+quoka_status ensure_lds(const Problem& p) {
+  static std::mutex mu;
+  static bool done[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QUOKA_EHIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(QUOKA_EUNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (done[dev]) return QUOKA_OK;
+  int max_lds = 0;
+  if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+      hipSuccess)
+    return fail(QUOKA_EHIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed");
+  const int need = kScoreBins * 4 + QUOKA_MAX_Q_BUDGET * 128 * 4;
+  if (max_lds < need)
+    return fail(QUOKA_EUNSUPPORTED, "device offers %d bytes of LDS per workgroup, scorer needs %d",
+                max_lds, need);
+  const hipError_t e = set_scorer_lds_limit(need);
+  if (e != hipSuccess)
+    return fail(QUOKA_EHIP, "hipFuncSetAttribute(scorer LDS): %s", hipGetErrorString(e));
+  done[dev] = true;
+  return QUOKA_OK;
+}
+
+quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Problem* p) {
+  if (!sh) return fail(QUOKA_EINVAL, "shape is null");
+  if (sh->num_seqs < 1) return fail(QUOKA_EINVAL, "num_seqs=%d must be >= 1", sh->num_seqs);
+  if (sh->num_q_heads < 1 || sh->num_kv_heads < 1)
+    return fail(QUOKA_EINVAL, "head counts must be >= 1 (H_q=%d, H_kv=%d)", sh->num_q_heads,
+                sh->num_kv_heads);
+  if (sh->num_q_heads % sh->num_kv_heads)
+    return fail(QUOKA_EINVAL, "num_q_heads=%d is not a multiple of num_kv_heads=%d",
+                sh->num_q_heads, sh->num_kv_heads);
+  if (sh->dtype != QUOKA_F32 && sh->dtype != QUOKA_BF16)
+    return fail(QUOKA_EINVAL, "dtype=%d is not a quoka_dtype", (int)sh->dtype);
+  if (sh->head_dim != 64 && sh->head_dim != 128)
+    return fail(QUOKA_EUNSUPPORTED, "head_dim=%d (built: 64, 128)", sh->head_dim);
+  if (!sh->cu_chunk || !sh->cu_hist || !sh->cu_chunk_host || !sh->cu_hist_host)
+    return fail(QUOKA_EINVAL, "cu_chunk / cu_hist device and host arrays must all be given");
+  if (q_budget < 1) return fail(QUOKA_EINVAL, "q_budget=%d must be >= 1", q_budget);
+  if (q_budget > QUOKA_MAX_Q_BUDGET)
+    return fail(QUOKA_EUNSUPPORTED, "q_budget=%d exceeds %d", q_budget, QUOKA_MAX_Q_BUDGET);
+  if (kv_budget < 1) return fail(QUOKA_EINVAL, "kv_budget=%d must be >= 1", kv_budget);
+  const int S = sh->num_seqs;
+  if (sh->cu_chunk_host[0] != 0 || sh->cu_hist_host[0] != 0)
+    return fail(QUOKA_EINVAL, "cu_chunk_host[0] and cu_hist_host[0] must be 0");
+  p->S = S;
+  p->Hq = sh->num_q_heads;
+  p->Hkv = sh->num_kv_heads;
+  p->G = p->Hq / p->Hkv;
+  p->D = sh->head_dim;
+  p->dtype = sh->dtype;
+  p->cu_chunk = sh->cu_chunk;
+  p->cu_hist = sh->cu_hist;
+  p->cu_chunk_h = sh->cu_chunk_host;
+  p->cu_hist_h = sh->cu_hist_host;
+  p->NQT = p->NSB = p->NKT = 0;
+  p->maxC = p->maxL = 0;
+  for (int s = 0; s < S; ++s) {
+    const int64_t C = (int64_t)sh->cu_chunk_host[s + 1] - sh->cu_chunk_host[s];
+    const int64_t L = (int64_t)sh->cu_hist_host[s + 1] - sh->cu_hist_host[s];
+    if (C < 0 || L < 0)
+      return fail(QUOKA_EINVAL, "cu offsets decrease at sequence %d", s);
+    p->NQT += (C + kQprepTokens - 1) / kQprepTokens;
+    p->NSB += (L + kScoreKeys - 1) / kScoreKeys;
+    p->NKT += (L + kTopbKeys - 1) / kTopbKeys;
+    p->maxC = std::max<int>(p->maxC, (int)C);
+    p->maxL = std::max<int>(p->maxL, (int)L);
+  }
+  p->TC = sh->cu_chunk_host[S];
+  p->TL = sh->cu_hist_host[S];
+  // element offsets are int64 in the kernels; per-row counts must fit int32
+  if (p->TC * p->Hq > INT32_MAX || p->TL * p->Hkv > INT32_MAX)
+    return fail(QUOKA_EUNSUPPORTED, "token totals too large");
+  if ((int64_t)p->maxC * p->G > INT32_MAX) return fail(QUOKA_EUNSUPPORTED, "chunk too long");
+  p->q_budget = q_budget;
+  p->kv_budget = kv_budget;
+  p->nq_pad = (q_budget + 15) / 16 * 16;
+  return QUOKA_OK;
+}
+
+}  // namespace
+
+Workspace workspace_layout(const Problem& p) {
+  Workspace w;
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  const size_t elem = p.dtype == QUOKA_BF16 ? 2 : 4;
+  const size_t SH = (size_t)p.S * p.Hkv;
+  w.plan = take(3 * (size_t)(p.S + 1) * 4);
+  w.g = take((size_t)p.TC * p.Hkv * p.D * 4);
+  w.gpart = take((size_t)p.NQT * p.Hkv * p.D * 8);
+  w.qcos = take((size_t)p.Hkv * p.TC * 4);
+  w.qidx = take(SH * p.q_budget * 4);
+  w.gsel = take(SH * p.nq_pad * p.D * 4);
+  w.scores = take((size_t)p.Hkv * p.TL * 4);
+  w.zero_begin = o;
+  w.hist = take(SH * kScoreBins * 4);
+  w.ccount = take(SH * 4);
+  w.chcount = take((size_t)p.Hkv * p.NKT * 4);
+  w.zero_end = o;
+  w.thr = take(SH * sizeof(Threshold));
+  w.cand = take((size_t)p.Hkv * p.TL * 8);
+  w.gtcount = take((size_t)p.Hkv * p.NKT * 4);
+  w.select_end = o;
+  w.selidx = take(SH * p.kv_budget * 4);
+  w.ksel = take(SH * p.kv_budget * p.D * elem);
+  w.vsel = take(SH * p.kv_budget * p.D * elem);
+  w.total = o;
+  return w;
+}
+
+}  // namespace quoka
+
+using namespace quoka;
+
+namespace {
+
+quoka_status run_select(const Problem& p, const Workspace& w, const void* q, const void* k_hist,
+                        int32_t* sel_idx, int32_t* q_idx_opt, float* qcos_opt, float* scores_opt,
+                        char* ws, hipStream_t st) {
+  quoka_status rc = ensure_lds(p);
+  if (rc != QUOKA_OK) return rc;
+  float* qcos = qcos_opt ? qcos_opt : (float*)(ws + w.qcos);
+  float* scores = scores_opt ? scores_opt : (float*)(ws + w.scores);
+  int32_t* qidx = q_idx_opt ? q_idx_opt : (int32_t*)(ws + w.qidx);
+  if ((rc = hip_check(launch_plan(p, ws, w, st), "plan", st))) return rc;
+  if ((rc = hip_check(launch_qprep(p, q, ws, w, qcos, st), "qprep", st))) return rc;
+  if ((rc = hip_check(launch_qselect(p, ws, w, qcos, qidx, st), "qselect", st))) return rc;
+  if ((rc = hip_check(launch_scorer(p, k_hist, ws, w, scores, st), "scorer", st))) return rc;
+  return hip_check(launch_topb(p, ws, w, scores, sel_idx, st), "topb", st);
+}
+
+#define QUOKA_NEED(ptr, total)                                                          \
+  do {                                                                                  \
+    if (!(ptr) && (total) > 0) return fail(QUOKA_EINVAL, "%s is null", #ptr);           \
+    if ((ptr) && !aligned16(ptr)) return fail(QUOKA_EINVAL, "%s is not 16-byte aligned", #ptr); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+quoka_status quoka_workspace_bytes(const quoka_shape* shape, int32_t q_budget,
+                                   int32_t kv_budget, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(QUOKA_EINVAL, "bytes is null");
+  Problem p;
+  quoka_status rc = make_problem(shape, q_budget, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  *bytes = workspace_layout(p).total;
+  return QUOKA_OK;
+}
+
+quoka_status quoka_select(const quoka_shape* shape, const void* q, const void* k_hist,
+                          int32_t q_budget, int32_t kv_budget, int32_t* sel_idx,
+                          int32_t* q_idx_opt, float* qcos_opt, float* scores_opt, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, q_budget, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(q, p.TC);
+  QUOKA_NEED(k_hist, p.TL);
+  QUOKA_NEED(sel_idx, 1);
+  if (!ws) return fail(QUOKA_EWORKSPACE, "workspace is null");
+  if (!aligned16(ws)) return fail(QUOKA_EINVAL, "workspace is not 16-byte aligned");
+  const Workspace w = workspace_layout(p);
+  if (ws_bytes < w.total)
+    return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  return run_select(p, w, q, k_hist, sel_idx, q_idx_opt, qcos_opt, scores_opt, (char*)ws,
+                    stream);
+}
+
+quoka_status quoka_gather(const quoka_shape* shape, const void* k_hist, const void* v_hist,
+                          const int32_t* sel_idx, int32_t kv_budget, void* k_sel, void* v_sel,
+                          hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, 1, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(k_hist, p.TL);
+  QUOKA_NEED(v_hist, p.TL);
+  QUOKA_NEED(sel_idx, 1);
+  QUOKA_NEED(k_sel, 1);
+  QUOKA_NEED(v_sel, 1);
+  return hip_check(launch_gather(p, k_hist, v_hist, sel_idx, k_sel, v_sel, stream), "gather",
+                   stream);
+}
+
+quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q, const void* k_sel,
+                              const void* v_sel, int32_t kv_budget, const void* k_chunk,
+                              const void* v_chunk, float softmax_scale, void* out,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, 1, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(q, p.TC);
+  QUOKA_NEED(k_sel, 1);
+  QUOKA_NEED(v_sel, 1);
+  QUOKA_NEED(k_chunk, p.TC);
+  QUOKA_NEED(v_chunk, p.TC);
+  QUOKA_NEED(out, p.TC);
+  if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
+  return hip_check(launch_attention(p, q, k_sel, v_sel, k_chunk, v_chunk, scale, out, stream),
+                   "attention", stream);
+}
+
+quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q, const void* k_hist,
+                                 const void* v_hist, const void* k_chunk, const void* v_chunk,
+                                 int32_t q_budget, int32_t kv_budget, float softmax_scale,
+                                 void* out, int32_t* sel_idx_opt, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, q_budget, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(q, p.TC);
+  QUOKA_NEED(k_hist, p.TL);
+  QUOKA_NEED(v_hist, p.TL);
+  QUOKA_NEED(k_chunk, p.TC);
+  QUOKA_NEED(v_chunk, p.TC);
+  QUOKA_NEED(out, p.TC);
+  if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
+  if (!ws) return fail(QUOKA_EWORKSPACE, "workspace is null");
+  if (!aligned16(ws)) return fail(QUOKA_EINVAL, "workspace is not 16-byte aligned");
+  const Workspace w = workspace_layout(p);
+  if (ws_bytes < w.total)
+    return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  char* base = (char*)ws;
+  int32_t* sel = sel_idx_opt ? sel_idx_opt : (int32_t*)(base + w.selidx);
+  rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
+  if (rc != QUOKA_OK) return rc;
+  void* ks = base + w.ksel;
+  void* vs = base + w.vsel;
+  rc = hip_check(launch_gather(p, k_hist, v_hist, sel, ks, vs, stream), "gather", stream);
+  if (rc != QUOKA_OK) return rc;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
+  return hip_check(launch_attention(p, q, ks, vs, k_chunk, v_chunk, scale, out, stream),
+                   "attention", stream);
+}
+
+const char* quoka_strerror(quoka_status status) {
+  switch (status) {
+    case QUOKA_OK: return "success";
+    case QUOKA_EINVAL: return "invalid argument";
+    case QUOKA_EUNSUPPORTED: return "unsupported configuration";
+    case QUOKA_EWORKSPACE: return "workspace missing or too small";
+    case QUOKA_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* quoka_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Device helpers shared by the QUOKA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace quoka {
+
+constexpr int kWave = 64;
+
+// ---- element conversion --------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// ---- wave reductions (64 lanes, result in every lane) --------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---- order-preserving keys -------------------------------------------------
+// Monotone map float -> uint32: a < b (as floats) <=> key(a) < key(b); -0 and
+// +0 map to the same key. NaN is outside the contract.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Linear histogram bin of a score in [-1, 1] (cosine-derived scores are
+// bounded). Monotone non-decreasing in s; out-of-range values clamp.
+constexpr int kScoreBins = 2048;
+__device__ __forceinline__ int score_bin(float s) {
+  float x = (s + 1.0f) * (0.5f * kScoreBins);
+  x = fminf(fmaxf(x, 0.0f), (float)(kScoreBins - 1));
+  return (int)x;
+}
+
+// Largest s in [0, n) with off[s] <= v, for non-decreasing off[0..n].
+__device__ __forceinline__ int upper_seq(const int32_t* off, int n, int v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace quoka

@@ -1,0 +1,84 @@
+// Host-side plumbing shared by the launchers and the C ABI: the workspace
+// layout, the per-call problem description and the launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "quoka.h"
+
+namespace quoka {
+
+// Tilings (all per sequence; tiles never straddle two sequences).
+constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
+constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup
+constexpr int kTopbKeys = 2048;      // history keys per top-B workgroup
+constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
+
+struct Problem {
+  int S, Hq, Hkv, G, D;
+  quoka_dtype dtype;
+  const int32_t* cu_chunk;   // device
+  const int32_t* cu_hist;    // device
+  const int32_t* cu_chunk_h; // host
+  const int32_t* cu_hist_h;  // host
+  int64_t TC, TL;            // total chunk tokens, total history keys
+  int64_t NQT, NSB, NKT;     // total qprep / scorer / top-B tiles over sequences
+  int maxC, maxL;            // longest chunk, longest history
+  int q_budget, kv_budget, nq_pad;
+};
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct Workspace {
+  size_t plan;      // int32 qt_off[S+1], sb_off[S+1], kt_off[S+1]
+  size_t g;         // float [TC, Hkv, D]  pre-aggregated queries
+  size_t gpart;     // double [NQT, Hkv, D] per-tile sums of g
+  size_t qcos;      // float [Hkv, TC]
+  size_t qidx;      // int32 [S, Hkv, q_budget]
+  size_t gsel;      // 4 B x [S, Hkv, nq_pad, D]  kept group queries for the scorer
+  size_t scores;    // float [Hkv, TL]
+  size_t hist;      // uint32 [S, Hkv, kScoreBins]
+  size_t thr;       // Threshold [S, Hkv]
+  size_t ccount;    // uint32 [S, Hkv] candidate counts
+  size_t cand;      // uint64 [Hkv, TL] candidates
+  size_t gtcount;   // uint32 [Hkv, NKT] keys above the threshold bin per tile
+  size_t chcount;   // uint32 [Hkv, NKT] chosen candidates per tile
+  size_t selidx;    // int32 [S, Hkv, B]  (prefill path)
+  size_t ksel;      // elem [S, Hkv, B, D] (prefill path)
+  size_t vsel;      // elem [S, Hkv, B, D] (prefill path)
+  size_t select_end, total;
+  size_t zero_begin, zero_end;  // [hist .. chcount] region cleared per call
+};
+
+struct Threshold {
+  int32_t bstar;        // bin holding the B_eff-th score; -1 = keep everything
+  int32_t above;        // keys in bins above bstar
+  int32_t need;         // keys still to take from bin bstar
+  int32_t pad;
+  uint64_t t64;         // smallest chosen (key << 32 | ~index) inside bin bstar
+};
+
+Workspace workspace_layout(const Problem& p);
+
+// Launchers (enqueue only; return hipGetLastError()).
+// Raise the dynamic-LDS limit of the scorer kernels (they hold the kept
+// queries and a score histogram on chip).
+hipError_t set_scorer_lds_limit(int bytes);
+
+hipError_t launch_plan(const Problem& p, char* ws, const Workspace& w, hipStream_t st);
+hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
+                        float* qcos, hipStream_t st);
+hipError_t launch_qselect(const Problem& p, char* ws, const Workspace& w, const float* qcos,
+                          int32_t* qidx, hipStream_t st);
+hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const Workspace& w,
+                         float* scores, hipStream_t st);
+hipError_t launch_topb(const Problem& p, char* ws, const Workspace& w, const float* scores,
+                       int32_t* sel_idx, hipStream_t st);
+hipError_t launch_gather(const Problem& p, const void* k_hist, const void* v_hist,
+                         const int32_t* sel_idx, void* k_sel, void* v_sel, hipStream_t st);
+hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
+                            const void* v_sel, const void* k_chunk, const void* v_chunk,
+                            float scale, void* out, hipStream_t st);
+
+}  // namespace quoka

@@ -1,0 +1,225 @@
+// K3: stream the history keys once and score them against the kept queries.
+//   s_i = max_{t in S_h} g_t . k_i / |k_i|
+// which is the max over kept tokens of the mean over the group's heads of the
+// per-head cosines (g_t is the mean of the token's unit query heads).
+// Sources: QUOKA paper summary (hw-hk.tistory.com/367), "Scoring via Cosine
+// Similarity" and "Aggregation Across Queries and KV Groups" (max over the
+// query axis, mean over the GQA axis, pre-aggregation); "QUOKA Explained",
+// "Letting those queries score the history", "Why take the maximum".
+//
+// The epilogue also builds the first-level histogram of the top-B select
+// (linear bins over [-1, 1]) so that the scores are not re-read for it.
+#include "common.h"
+#include "internal.h"
+
+namespace quoka {
+
+// bf16 keys, MFMA v_mfma_f32_16x16x32_bf16.
+//   A = kept queries [16 x 32 d] from LDS (pre-laid-out by the query select as
+//       hi and lo bf16 terms of the fp32 g, so g ~ hi + lo to 2^-16),
+//   B = keys [32 d x 16 keys] straight from global memory (each lane reads 16
+//       contiguous bytes of one key row; 4 lanes cover 64 B of a row),
+//   C = [16 queries x 16 keys]; lane l holds key column l%16, so the max over
+//       queries is a per-lane max followed by two cross-lane steps.
+// One workgroup = 4 waves = up to kScoreKeys keys of one (sequence, KV head);
+// each wave takes 64 keys (4 blocks of 16) per iteration.
+template <int D>
+__global__ __launch_bounds__(256) void scorer_mfma_kernel(
+    const bf16* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
+    const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
+    int64_t TL, int q_budget, int nq_pad, const bf16x8* __restrict__ gsel,
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  constexpr int NDS = D / 32;  // d-steps per key
+  const int blk = blockIdx.x, h = blockIdx.y;
+  const int32_t* sb_off = plan + (S + 1);
+  const int s = upper_seq(sb_off, S, blk);
+  const int k_begin = (blk - sb_off[s]) * kScoreKeys;
+  const int h_off = cu_hist[s];
+  const int L = cu_hist[s + 1] - h_off;
+  const int k_end = min(L, k_begin + kScoreKeys);
+  const int n = min(q_budget, cu_chunk[s + 1] - cu_chunk[s]);
+  const int nqb = (n + 15) / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int prob = s * Hkv + h;
+
+  extern __shared__ char smem[];
+  uint32_t* lhist = (uint32_t*)smem;                       // kScoreBins
+  bf16x8* lg = (bf16x8*)(smem + kScoreBins * 4);           // nqb * NDS * 2 * 64
+  for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
+  {
+    const bf16x8* src = gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64;
+    for (int i = threadIdx.x; i < nqb * NDS * 2 * 64; i += 256) lg[i] = src[i];
+  }
+  __syncthreads();
+
+  float* srow = scores + (int64_t)h * TL + h_off;
+  for (int it = 0; it < kScoreKeys / 256; ++it) {
+    const int k0 = k_begin + it * 256 + wave * 64;
+    if (k0 >= k_end) break;
+    bf16x8 b[4][NDS];
+    float nsq[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = k0 + kb * 16 + (lane & 15);
+      const bool ok = key < k_end;
+      const bf16* row = k_hist + ((int64_t)(h_off + (ok ? key : 0)) * Hkv + h) * D + (lane >> 4) * 8;
+      float ss = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        bf16x8 v = *(const bf16x8*)(row + ds * 32);
+        if (!ok) v = (bf16x8){};
+        b[kb][ds] = v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)v[e];
+          ss = fmaf(x, x, ss);
+        }
+      }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      nsq[kb] = ss;
+    }
+    float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int qb = 0; qb < nqb; ++qb) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) acc[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 ahi = lg[((qb * NDS + ds) * 2 + 0) * 64 + lane];
+        const bf16x8 alo = lg[((qb * NDS + ds) * 2 + 1) * 64 + lane];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b[kb][ds], acc[kb], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b[kb][ds], acc[kb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        m[kb] = fmaxf(m[kb], fmaxf(fmaxf(acc[kb][0], acc[kb][1]), fmaxf(acc[kb][2], acc[kb][3])));
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      m[kb] = fmaxf(m[kb], __shfl_xor(m[kb], 16, 64));
+      m[kb] = fmaxf(m[kb], __shfl_xor(m[kb], 32, 64));
+    }
+    // lane l stores key k0 + l: its column is l%16 of key block l/16
+    const int kb = lane >> 4;
+    const float mm = kb == 0 ? m[0] : kb == 1 ? m[1] : kb == 2 ? m[2] : m[3];
+    const float ns = kb == 0 ? nsq[0] : kb == 1 ? nsq[1] : kb == 2 ? nsq[2] : nsq[3];
+    const int key = k0 + lane;
+    if (key < k_end) {
+      const float sc = (n > 0 && ns > 0.f) ? mm / sqrtf(ns) : 0.f;
+      srow[key] = sc;
+      atomicAdd(&lhist[score_bin(sc)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = hist + (int64_t)prob * kScoreBins;
+  for (int i = threadIdx.x; i < kScoreBins; i += 256) {
+    const uint32_t c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// fp32 keys (and any dtype as a reference path): one key per thread, kept
+// queries as fp32 rows in LDS read by broadcast.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void scorer_valu_kernel(
+    const T* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
+    const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
+    int64_t TL, int q_budget, int nq_pad, const float* __restrict__ gsel,
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+  const int blk = blockIdx.x, h = blockIdx.y;
+  const int32_t* sb_off = plan + (S + 1);
+  const int s = upper_seq(sb_off, S, blk);
+  const int k_begin = (blk - sb_off[s]) * kScoreKeys;
+  const int h_off = cu_hist[s];
+  const int L = cu_hist[s + 1] - h_off;
+  const int k_end = min(L, k_begin + kScoreKeys);
+  const int n = min(q_budget, cu_chunk[s + 1] - cu_chunk[s]);
+  const int prob = s * Hkv + h;
+
+  extern __shared__ char smem[];
+  uint32_t* lhist = (uint32_t*)smem;
+  float* lg = (float*)(smem + kScoreBins * 4);  // n x D
+  for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
+  const float* src = gsel + (int64_t)prob * nq_pad * D;
+  for (int i = threadIdx.x; i < n * D; i += 256) lg[i] = src[i];
+  __syncthreads();
+
+  float* srow = scores + (int64_t)h * TL + h_off;
+  for (int key = k_begin + threadIdx.x; key < k_end; key += 256) {
+    const T* row = k_hist + ((int64_t)(h_off + key) * Hkv + h) * D;
+    float k[D];
+    float ss = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      k[d] = to_f32(row[d]);
+      ss = fmaf(k[d], k[d], ss);
+    }
+    float m = -INFINITY;
+    for (int r = 0; r < n; ++r) {
+      const float* gr = lg + r * D;
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dot = fmaf(gr[d], k[d], dot);
+      m = fmaxf(m, dot);
+    }
+    const float sc = (n > 0 && ss > 0.f) ? m / sqrtf(ss) : 0.f;
+    srow[key] = sc;
+    atomicAdd(&lhist[score_bin(sc)], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = hist + (int64_t)prob * kScoreBins;
+  for (int i = threadIdx.x; i < kScoreBins; i += 256) {
+    const uint32_t c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+hipError_t set_scorer_lds_limit(int bytes) {
+  const void* fns[] = {(const void*)scorer_mfma_kernel<128>, (const void*)scorer_mfma_kernel<64>,
+                       (const void*)scorer_valu_kernel<float, 128>,
+                       (const void*)scorer_valu_kernel<float, 64>};
+  for (const void* f : fns) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const Workspace& w,
+                         float* scores, hipStream_t st) {
+  if (p.NSB == 0) return hipSuccess;
+  dim3 grid((unsigned)p.NSB, (unsigned)p.Hkv);
+  const int32_t* plan = (const int32_t*)(ws + w.plan);
+  uint32_t* hist = (uint32_t*)(ws + w.hist);
+  if (p.dtype == QUOKA_BF16) {
+    const size_t lds = kScoreBins * 4 + (size_t)p.nq_pad * p.D * 4;
+    const bf16x8* gsel = (const bf16x8*)(ws + w.gsel);
+    if (p.D == 128)
+      hipLaunchKernelGGL((scorer_mfma_kernel<128>), grid, dim3(256), lds, st, (const bf16*)k_hist,
+                         p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL, p.q_budget, p.nq_pad,
+                         gsel, scores, hist);
+    else
+      hipLaunchKernelGGL((scorer_mfma_kernel<64>), grid, dim3(256), lds, st, (const bf16*)k_hist,
+                         p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL, p.q_budget, p.nq_pad,
+                         gsel, scores, hist);
+  } else {
+    const size_t lds = kScoreBins * 4 + (size_t)p.q_budget * p.D * 4;
+    const float* gsel = (const float*)(ws + w.gsel);
+    if (p.D == 128)
+      hipLaunchKernelGGL((scorer_valu_kernel<float, 128>), grid, dim3(256), lds, st,
+                         (const float*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,
+                         p.q_budget, p.nq_pad, gsel, scores, hist);
+    else
+      hipLaunchKernelGGL((scorer_valu_kernel<float, 64>), grid, dim3(256), lds, st,
+                         (const float*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,
+                         p.q_budget, p.nq_pad, gsel, scores, hist);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace quoka

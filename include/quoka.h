@@ -1,0 +1,162 @@
+/*
+ * quoka.h - C ABI of the QUOKA per-chunk hot path on MI355X (gfx950).
+ *
+ * QUOKA ("QUOKA: Query-Oriented KV Selection For Efficient LLM Prefill")
+ * speeds up chunked prefill by letting each chunk attend to a small subset of
+ * the cached history. Per (sequence, KV head) the library
+ *   1. reduces the chunk's queries of the KV head's query heads to a mean
+ *      query and keeps the N_q queries least similar to it;
+ *   2. scores every history key by cosine similarity against the kept
+ *      queries, taking the max over kept tokens of the mean over the group's
+ *      heads, and keeps the top-B keys;
+ *   3. gathers the kept keys' K/V rows;
+ *   4. runs softmax attention of every chunk query (original heads) over the
+ *      kept history plus the chunk's own keys under a causal mask.
+ * Sources: the QUOKA paper summary (hw-hk.tistory.com/367), sections "QUOKA
+ * Method" and "Background > Chunked prefill", and "QUOKA Explained: Choosing
+ * Which KV History Attention Should Read" (reactapp.top).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are DEVICE pointers unless their name ends in _host. The caller
+ * owns every buffer; the library never allocates or frees memory and keeps no
+ * state between calls except a per-device cache of device properties, so calls
+ * on different streams may run concurrently as long as they share no output
+ * or workspace buffer.
+ *
+ * Layouts are token-major and contiguous (elements of `dtype`):
+ *   q                [sum_s C_s, H_q,  d]   chunk queries
+ *   k_hist, v_hist   [sum_s L_s, H_kv, d]   cached history K/V (never modified)
+ *   k_chunk, v_chunk [sum_s C_s, H_kv, d]   the chunk's own K/V
+ *   out              [sum_s C_s, H_q,  d]
+ *   k_sel, v_sel     [S, H_kv, B, d]        gathered rows
+ *   sel_idx          [S, H_kv, B]   int32   kept history positions (0-based
+ *                                           within the sequence), ascending,
+ *                                           -1 padding past B_eff
+ * Query head j belongs to KV head j / (H_q / H_kv) (contiguous GQA groups).
+ * Per sequence the budgets are clamped to the data:
+ *   N_q,eff = min(q_budget, C_s), B_eff = min(kv_budget, L_s).
+ * Ties in either selection go to the lower token / key index, so every result
+ * is unique. Inputs must be finite.
+ *
+ * Errors: validation runs on the host before anything is enqueued and returns
+ * QUOKA_EINVAL / QUOKA_EUNSUPPORTED / QUOKA_EWORKSPACE without touching the
+ * GPU; quoka_last_error() then names the offending argument. A failed launch
+ * returns QUOKA_EHIP. Device faults surface asynchronously, as with any HIP
+ * call; set the environment variable QUOKA_SYNC=1 to synchronize the stream
+ * after every launch and report them as QUOKA_EHIP.
+ */
+#ifndef QUOKA_H
+#define QUOKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum quoka_status {
+  QUOKA_OK = 0,
+  QUOKA_EINVAL = 1,        /* a null pointer, negative size or inconsistent offsets */
+  QUOKA_EUNSUPPORTED = 2,  /* well-formed but outside what is built (head_dim, budget) */
+  QUOKA_EWORKSPACE = 3,    /* workspace null or smaller than quoka_workspace_bytes() */
+  QUOKA_EHIP = 4           /* a HIP launch or query failed */
+} quoka_status;
+
+typedef enum quoka_dtype {
+  QUOKA_F32 = 0,           /* fp32 everywhere, VALU kernels */
+  QUOKA_BF16 = 1           /* bf16 Q/K/V/out; fp32 arithmetic; MFMA kernels */
+} quoka_dtype;
+
+/* Problem shape. head_dim must be 64 or 128; num_q_heads a multiple of
+ * num_kv_heads. cu_chunk / cu_hist are prefix offsets of the chunk and
+ * history lengths ([0] == 0, non-decreasing). The device and host copies must
+ * hold the same values: the host copy sizes the launch grids, the kernels read
+ * the device copy. */
+typedef struct quoka_shape {
+  int32_t num_seqs;               /* S >= 1 */
+  int32_t num_q_heads;            /* H_q */
+  int32_t num_kv_heads;           /* H_kv */
+  int32_t head_dim;               /* d */
+  quoka_dtype dtype;
+  const int32_t* cu_chunk;        /* device [S + 1] */
+  const int32_t* cu_hist;         /* device [S + 1] */
+  const int32_t* cu_chunk_host;   /* host   [S + 1] */
+  const int32_t* cu_hist_host;    /* host   [S + 1] */
+} quoka_shape;
+
+/* Largest q_budget the scorer holds on chip (kept queries per KV head). */
+#define QUOKA_MAX_Q_BUDGET 128
+
+/* Bytes of device workspace quoka_select / quoka_prefill_chunk need for this
+ * shape and these budgets (written to *bytes). */
+quoka_status quoka_workspace_bytes(const quoka_shape* shape, int32_t q_budget,
+                                   int32_t kv_budget, size_t* bytes);
+
+/* Selection: steps 1 and 2 above ("QUOKA Method": query subselection,
+ * cosine scoring, aggregation across queries and KV groups; "QUOKA Explained":
+ * "Pick the queries that disagree with the crowd" through "From scores to a
+ * smaller KV set").
+ *   q, k_hist    inputs (dtype of shape)
+ *   q_budget     N_q, 1 .. QUOKA_MAX_Q_BUDGET
+ *   kv_budget    B >= 1
+ *   sel_idx      out [S, H_kv, kv_budget] int32
+ *   q_idx_opt    optional out [S, H_kv, q_budget] int32: kept chunk tokens,
+ *                ascending, -1 padding
+ *   qcos_opt     optional out [H_kv, sum C] float: each token's cosine to its
+ *                chunk's mean query
+ *   scores_opt   optional out [H_kv, sum L] float: each history key's score
+ *   ws, ws_bytes device workspace of at least quoka_workspace_bytes() bytes;
+ *                its contents on entry do not matter
+ */
+quoka_status quoka_select(const quoka_shape* shape, const void* q,
+                          const void* k_hist, int32_t q_budget,
+                          int32_t kv_budget, int32_t* sel_idx,
+                          int32_t* q_idx_opt, float* qcos_opt,
+                          float* scores_opt, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Gather: step 3 ("QUOKA Explained", "From scores to a smaller KV set": a kept
+ * key brings its value). Row b of (s, h) in k_sel / v_sel is row
+ * sel_idx[s, h, b] of sequence s, head h of k_hist / v_hist; rows whose index
+ * is -1 are written as zeros. Indices must be -1 or in [0, L_s). */
+quoka_status quoka_gather(const quoka_shape* shape, const void* k_hist,
+                          const void* v_hist, const int32_t* sel_idx,
+                          int32_t kv_budget, void* k_sel, void* v_sel,
+                          hipStream_t stream);
+
+/* Chunk attention: step 4 ("Background > Chunked prefill"; "QUOKA Method":
+ * the reduced KV set goes to a dense attention kernel). Query row (t, j) of
+ * sequence s attends to the first B_eff rows of k_sel / v_sel[s, j / G] and to
+ * the chunk's keys 0..t (diagonal included).
+ *   softmax_scale <= 0 selects 1 / sqrt(d). */
+quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q,
+                              const void* k_sel, const void* v_sel,
+                              int32_t kv_budget, const void* k_chunk,
+                              const void* v_chunk, float softmax_scale,
+                              void* out, hipStream_t stream);
+
+/* The whole hot path (select, gather into the workspace, attend) in one call.
+ * sel_idx_opt, when not null, receives the kept indices as in quoka_select. */
+quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q,
+                                 const void* k_hist, const void* v_hist,
+                                 const void* k_chunk, const void* v_chunk,
+                                 int32_t q_budget, int32_t kv_budget,
+                                 float softmax_scale, void* out,
+                                 int32_t* sel_idx_opt, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* quoka_strerror(quoka_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* quoka_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUOKA_H */

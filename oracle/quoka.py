@@ -51,7 +51,7 @@ import numpy as np
 __all__ = [
     "unit", "cosine_matrix", "group_query", "query_cosines",
     "lowest_cosine_queries", "key_scores", "top_b_keys", "attend_rows",
-    "select_for_head", "prefill_chunk", "effective_budgets",
+    "attend_chunk", "select_for_head", "prefill_chunk", "effective_budgets",
 ]
 
 
@@ -215,8 +215,13 @@ def attend_rows(q_rows, t_rows, k_sel, v_sel, k_chunk, v_chunk,
     return out
 
 
-def _attend_chunk(q_head, k_sel, v_sel, k_chunk, v_chunk, scale):
-    """All C rows of one query head at once; same definition as attend_rows."""
+def attend_chunk(q_head, k_sel, v_sel, k_chunk, v_chunk, scale):
+    """All C rows of one query head at once; same definition as attend_rows.
+
+    q_head [C, d]; k_sel, v_sel [B_eff, d]; k_chunk, v_chunk [C, d] -> [C, d].
+    """
+    q_head, k_sel, v_sel = _f64(q_head), _f64(k_sel), _f64(v_sel)
+    k_chunk, v_chunk = _f64(k_chunk), _f64(v_chunk)
     C = q_head.shape[0]
     Bs = k_sel.shape[0]
     keys = np.concatenate([k_sel, k_chunk], axis=0)
@@ -307,7 +312,7 @@ def prefill_chunk(q, k_hist, v_hist, k_chunk, v_chunk, cu_chunk, cu_hist,
                 continue
             ks, vs = k_h[r["I"]], v_hist[h0:h1, h, :][r["I"]]
             for j in range(h * G, (h + 1) * G):
-                out[c0:c1, j, :] = _attend_chunk(
+                out[c0:c1, j, :] = attend_chunk(
                     q[c0:c1, j, :], ks, vs, k_chunk[c0:c1, h, :],
                     v_chunk[c0:c1, h, :], scale)
     return {"out": out, "q_idx": q_idx, "sel_idx": sel_idx,

@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports what include/quoka.h
+declares, and validates arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import chunked_prefill_kv_amd as cpk
+from chunked_prefill_kv_amd import build as cbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "quoka.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cpk.LIB_PATH):
+        cbuild.build()
+    return cpk.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(quoka_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(cpk.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", cpk.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (quoka_\w+)", out))
+    assert set(_declared()) <= exported
+    for name in _declared():
+        assert hasattr(lib, name)
+
+
+def test_library_is_built_for_gfx950(lib):
+    out = subprocess.run(["strings", cpk.LIB_PATH], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+def _host_shape(cu_chunk, cu_hist, hq=8, hkv=2, d=128, dtype="bf16"):
+    return cpk.Shape(cu_chunk, cu_hist, hq, hkv, d, dtype, device="cpu")
+
+
+def _ws_status(shape, qb, kvb):
+    n = ctypes.c_size_t(0)
+    st = cpk.load_library().quoka_workspace_bytes(ctypes.byref(shape.c), qb, kvb,
+                                                  ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_grows_with_the_problem(lib):
+    st1, n1 = _ws_status(_host_shape([0, 100], [0, 1000]), 16, 64)
+    st2, n2 = _ws_status(_host_shape([0, 100, 300], [0, 1000, 5000]), 16, 64)
+    st3, n3 = _ws_status(_host_shape([0, 100], [0, 1000]), 32, 512)
+    assert (st1, st2, st3) == (0, 0, 0)
+    assert 0 < n1 < n2 and n1 < n3
+    assert n1 % 256 == 0
+
+
+@pytest.mark.parametrize("kw,qb,kvb,code", [
+    (dict(hq=6, hkv=4), 8, 8, cpk.QUOKA_EINVAL),          # H_q not a multiple of H_kv
+    (dict(d=96), 8, 8, cpk.QUOKA_EUNSUPPORTED),           # head_dim not built
+    (dict(), 0, 8, cpk.QUOKA_EINVAL),                     # q_budget < 1
+    (dict(), cpk.MAX_Q_BUDGET + 1, 8, cpk.QUOKA_EUNSUPPORTED),
+    (dict(), 8, 0, cpk.QUOKA_EINVAL),                     # kv_budget < 1
+])
+def test_workspace_validation(lib, kw, qb, kvb, code):
+    st, _ = _ws_status(_host_shape([0, 10], [0, 20], **kw), qb, kvb)
+    assert st == code
+    assert lib.quoka_last_error().decode()
+    assert lib.quoka_strerror(code).decode()
+
+
+def test_bad_offsets_are_rejected(lib):
+    assert _ws_status(_host_shape([0, 10, 5], [0, 20, 30]), 8, 8)[0] == cpk.QUOKA_EINVAL
+    assert _ws_status(_host_shape([1, 10], [0, 20]), 8, 8)[0] == cpk.QUOKA_EINVAL
+    bad = _host_shape([0, 10], [0, 20])
+    bad.c.num_seqs = 0
+    assert _ws_status(bad, 8, 8)[0] == cpk.QUOKA_EINVAL
+    bad = _host_shape([0, 10], [0, 20])
+    bad.c.dtype = 7
+    assert _ws_status(bad, 8, 8)[0] == cpk.QUOKA_EINVAL
+
+
+def test_select_rejects_missing_workspace_before_any_launch(lib):
+    shape = _host_shape([0, 10], [0, 20])
+    buf = np.zeros(4096, np.uint8)  # host memory: never dereferenced
+    p = buf.ctypes.data
+    st = lib.quoka_select(ctypes.byref(shape.c), p, p, 4, 8, p, None, None, None, None, 0, None)
+    assert st == cpk.QUOKA_EWORKSPACE
+    st = lib.quoka_select(ctypes.byref(shape.c), p, p, 4, 8, p, None, None, None, p, 16, None)
+    assert st == cpk.QUOKA_EWORKSPACE
+    assert "needs" in lib.quoka_last_error().decode()
+
+
+def test_null_and_misaligned_inputs_are_rejected(lib):
+    shape = _host_shape([0, 10], [0, 20])
+    buf = np.zeros(4096, np.uint8)
+    p = buf.ctypes.data + (16 - buf.ctypes.data % 16) % 16
+    st = lib.quoka_prefill_chunk(ctypes.byref(shape.c), None, p, p, p, p, 4, 8, 0.0, p, None, p,
+                                 1 << 30, None)
+    assert st == cpk.QUOKA_EINVAL and "q is null" in lib.quoka_last_error().decode()
+    st = lib.quoka_chunk_attn(ctypes.byref(shape.c), p + 2, p, p, 8, p, p, 0.0, p, None)
+    assert st == cpk.QUOKA_EINVAL and "aligned" in lib.quoka_last_error().decode()
+    st = lib.quoka_chunk_attn(ctypes.byref(shape.c), p, p, p, 8, p, p, float("nan"), p, None)
+    assert st == cpk.QUOKA_EINVAL
+    st = lib.quoka_gather(ctypes.byref(shape.c), p, p, None, 8, p, p, None)
+    assert st == cpk.QUOKA_EINVAL
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(cpk, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        cpk.load_library(str(tmp_path / "missing.so"))

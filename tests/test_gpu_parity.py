@@ -1,0 +1,136 @@
+"""GPU parity of every stage against the fp64 oracle, at sizes the oracle
+finishes in seconds (several tiles per kernel plus ragged tails), and the edge
+cases: empty history, one-token chunk, budgets above the data, the largest
+query budget, zero vectors, head_dim 64 and 128, GQA groups of 1, 2, 4 and 7.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_prefill_kv_amd as cpk
+import oracle
+from workloads import make_case, make_config
+
+from gpu_check import (upload, run_stages, check_selection, check_gather, check_attention,
+                       check_invariants, check_needles)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (seqs [(C, L)], H_q, H_kv, d, dtype, N_q, B, extra)
+    "fp32_d128_g2_ragged": ([(70, 3000), (1, 500), (33, 0), (130, 40)], 4, 2, 128, "fp32",
+                            8, 64, {}),
+    "fp32_d64_g1": ([(200, 2500)], 2, 2, 64, "fp32", 16, 300, {}),
+    "bf16_d128_g4_ragged": ([(300, 5000), (129, 2049), (64, 0), (1, 700)], 8, 2, 128, "bf16",
+                            20, 256, dict(scaled=True)),
+    "bf16_d128_g7_maxq": ([(200, 4100)], 14, 2, 128, "bf16", 128, 1000, {}),
+    "bf16_d64_g2": ([(100, 3000), (17, 1500)], 4, 2, 64, "bf16", 32, 300, {}),
+    "bf16_d128_g1_rope": ([(150, 2000)], 2, 2, 128, "bf16", 16, 128, dict(rope_base=1e6)),
+    "bf16_budget_above_data": ([(90, 50), (40, 500)], 8, 2, 128, "bf16", 200 // 2, 600, {}),
+    "bf16_needles": ([(256, 3000), (128, 1500)], 8, 2, 128, "bf16", 8, 32,
+                     dict(needles_per_head=4, outlier_needles=6.0)),
+}
+
+
+def _case(name, seed=1234):
+    seqs, hq, hkv, d, dt, nq, b, extra = CASES[name]
+    return make_case(seqs, hq, hkv, d, dt, nq, b, seed, name=name, **extra)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_stage_parity(name):
+    print(f"[gpu] stage parity {name}", flush=True)
+    w = _case(name)
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    check_invariants(w, r)
+    ties = check_selection(w, r)
+    check_gather(w, r)
+    err = check_attention(w, r)
+    print(f"[gpu] {name}: ties {ties}, attention max-abs {err:.3g}", flush=True)
+    if w.needles.shape[0]:
+        hit, total, in_s = check_needles(w, r)
+        assert in_s == total  # the outlier recipe puts every needle query in the kept set
+
+
+def test_fused_equals_stagewise():
+    """quoka_prefill_chunk runs the same kernels: bit-identical output."""
+    w = _case("bf16_d128_g4_ragged")
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    sel = torch.empty((w.num_seqs, w.num_kv_heads, w.budget), dtype=torch.int32, device="cuda")
+    out = cpk.prefill_chunk(shape, t["q"], t["k_hist"], t["v_hist"], t["k_chunk"],
+                            t["v_chunk"], w.n_q, w.budget, sel_idx=sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), r["sel_idx"])
+    assert np.array_equal(out.float().cpu().numpy(), r["out"])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = _case("bf16_d128_g7_maxq")
+    shape, t = upload(w)
+    ws = cpk.alloc_workspace(shape, w.n_q, w.budget)
+    outs = []
+    for _ in range(5):
+        sel = torch.empty((w.num_seqs, w.num_kv_heads, w.budget), dtype=torch.int32,
+                          device="cuda")
+        o = cpk.prefill_chunk(shape, t["q"], t["k_hist"], t["v_hist"], t["k_chunk"],
+                              t["v_chunk"], w.n_q, w.budget, sel_idx=sel, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((sel.cpu().numpy(), o.view(torch.int16).cpu().numpy()))
+    for a, b in outs[1:]:
+        assert np.array_equal(a, outs[0][0]) and np.array_equal(b, outs[0][1])
+
+
+def test_zero_vectors():
+    """Zero queries and keys: unit(0) = 0, so their cosines and scores are 0."""
+    w = make_case([(96, 800)], 8, 2, 128, "bf16", 16, 64, seed=99, name="zeros")
+    w.q[5] = 0.0                 # a whole token
+    w.q[7, 0:4] = 0.0            # one KV group of a token
+    w.k_hist[10:20, 1] = 0.0     # keys of head 1
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    check_invariants(w, r)
+    check_selection(w, r)
+    check_attention(w, r)
+    assert np.all(r["scores"][1, 10:20] == 0.0)
+
+
+def test_all_zero_chunk_keeps_lowest_tokens():
+    """All-zero queries: the mean query is 0, every cosine is 0, ties keep 0..N_q-1."""
+    w = make_case([(50, 300)], 4, 1, 128, "fp32", 6, 20, seed=5, name="zero_chunk")
+    w.q[:] = 0.0
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    assert r["q_idx"][0, 0].tolist() == list(range(6))
+    assert np.all(r["qcos"] == 0.0)
+    # every score is 0 too: the first B keys are kept
+    assert r["sel_idx"][0, 0].tolist() == list(range(20))
+
+
+def test_tiny_config_full_parity():
+    w = make_config("tiny")
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    check_invariants(w, r)
+    check_selection(w, r)
+    check_gather(w, r)
+    check_attention(w, r)
+    hit, total, in_s = check_needles(w, r)
+    print(f"[gpu] tiny needles kept {hit}/{total} ({in_s} aligned with kept queries)")
+
+
+def test_binding_rejects_wrong_inputs():
+    w = _case("fp32_d64_g1")
+    shape, t = upload(w)
+    with pytest.raises(ValueError):
+        cpk.select(shape, t["q"].to(torch.bfloat16), t["k_hist"], 8, 16)
+    with pytest.raises(cpk.QuokaError) as e:
+        cpk.select(shape, t["q"], t["k_hist"], 0, 16)
+    assert e.value.status == cpk.QUOKA_EINVAL
+    with pytest.raises(cpk.QuokaError) as e:
+        cpk.select(shape, t["q"], t["k_hist"], 8, 16,
+                   workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == cpk.QUOKA_EWORKSPACE

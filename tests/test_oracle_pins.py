@@ -332,7 +332,7 @@ def _mutations():
         "keep_lowest_scores": ("top_b_keys", lowest_scores),
         "tie_to_higher_index": ("top_b_keys", tie_high_index),
         "mask_without_diagonal": ("attend_rows", causal_strict),
-        "chunk_mask_without_diagonal": ("_attend_chunk", chunk_strict),
+        "chunk_mask_without_diagonal": ("attend_chunk", chunk_strict),
     }
 
 
