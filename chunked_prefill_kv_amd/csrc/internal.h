@@ -12,8 +12,8 @@ namespace quoka {
 
 // Tilings (all per sequence; tiles never straddle two sequences).
 constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
-constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup
-constexpr int kTopbKeys = 2048;      // history keys per top-B workgroup
+constexpr int kScoreKeys = 512;      // history keys per scorer workgroup
+constexpr int kTopbKeys = 512;       // history keys per top-B workgroup
 constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
 
 struct Problem {
@@ -56,7 +56,8 @@ struct Threshold {
   int32_t above;        // keys in bins above bstar
   int32_t need;         // keys still to take from bin bstar
   int32_t pad;
-  uint64_t t64;         // smallest chosen (key << 32 | ~index) inside bin bstar
+  uint64_t prefix;      // chosen candidates: (cand_key & mask) >= prefix
+  uint64_t mask;
 };
 
 Workspace workspace_layout(const Problem& p);

@@ -53,10 +53,15 @@ hipError_t launch_plan(const Problem& p, char* ws, const Workspace& w, hipStream
 // ---------------------------------------------------------------------------
 // K1a: g_t = mean_j unit(q_{t,j}) over the G query heads of KV head h, for a
 // tile of 64 tokens; also the tile's fp64 sum of g (for the mean query).
-// Lanes work in groups of 16 on one head row each (4 rows per instruction).
+// 16 waves; each wave owns 4 tokens and issues all their row loads before
+// reducing. Lanes work in groups of 16 on one head row (4 rows/instruction).
 // ---------------------------------------------------------------------------
+constexpr int kQprepThreads = 1024;
+constexpr int kQprepWaves = kQprepThreads / 64;
+constexpr int kTokPerWave = kQprepTokens / kQprepWaves;  // 4
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void qprep_g_kernel(
+__global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ plan, int S, int Hq, int Hkv, int G, float* __restrict__ g,
     double* __restrict__ gpart) {
@@ -64,120 +69,158 @@ __global__ __launch_bounds__(256) void qprep_g_kernel(
   const int tile = blockIdx.x, h = blockIdx.y;
   const int32_t* qt_off = plan;
   const int s = upper_seq(qt_off, S, tile);
-  const int t0 = (tile - qt_off[s]) * kQprepTokens;
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, sub = lane & 15;
+  const int tw = (tile - qt_off[s]) * kQprepTokens + wave * kTokPerWave;
 
-  double part[EPL];
+  float acc[kTokPerWave][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) part[e] = 0.0;
+  for (int i = 0; i < kTokPerWave; ++i)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
 
-  for (int i = 0; i < kQprepTokens / 4; ++i) {
-    const int t = t0 + wave * (kQprepTokens / 4) + i;
-    if (t >= C) break;  // uniform across the wave
-    float acc[EPL];
+  for (int j0 = 0; j0 < G; j0 += 4) {
+    const int j = j0 + grp;
+    float x[kTokPerWave][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    for (int j0 = 0; j0 < G; j0 += 4) {
-      const int j = j0 + grp;
-      float x[EPL];
-      if (j < G) {
-        const T* row = q + ((int64_t)(c_off + t) * Hq + (int64_t)h * G + j) * D + sub * EPL;
+    for (int i = 0; i < kTokPerWave; ++i) {
+      const int t = tw + i;
+      const bool ok = t < C && j < G;
+      const T* row = q + ((int64_t)(c_off + (ok ? t : 0)) * Hq + (int64_t)h * G + (ok ? j : 0)) * D +
+                     sub * EPL;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = to_f32(row[e]);
-      } else {
+      for (int e = 0; e < EPL; ++e) x[i][e] = ok ? to_f32(row[e]) : 0.f;
+    }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = 0.f;
-      }
+    for (int i = 0; i < kTokPerWave; ++i) {
       float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ss = fmaf(x[e], x[e], ss);
+      for (int e = 0; e < EPL; ++e) ss = fmaf(x[i][e], x[i][e], ss);
 #pragma unroll
       for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
       const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(x[e], inv, acc[e]);
+      for (int e = 0; e < EPL; ++e) acc[i][e] = fmaf(x[i][e], inv, acc[i][e]);
     }
+  }
+  double part[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) part[e] = 0.0;
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i) {
+    const int t = tw + i;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      acc[e] += __shfl_xor(acc[e], 16, 64);
-      acc[e] += __shfl_xor(acc[e], 32, 64);
-      acc[e] /= (float)G;
+      float v = acc[i][e];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      acc[i][e] = v / (float)G;
     }
-    if (grp == 0) {
+    if (grp == 0 && t < C) {
       float* dst = g + ((int64_t)(c_off + t) * Hkv + h) * D + sub * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        dst[e] = acc[e];
-        part[e] += (double)acc[e];
+        dst[e] = acc[i][e];
+        part[e] += (double)acc[i][e];
       }
     }
   }
-  __shared__ double red[4][D];
+  __shared__ double red[kQprepWaves][D];
   if (grp == 0) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) red[wave][sub * EPL + e] = part[e];
   }
   __syncthreads();
   if (threadIdx.x < D) {
-    const int i = threadIdx.x;
-    gpart[((int64_t)tile * Hkv + h) * D + i] = red[0][i] + red[1][i] + red[2][i] + red[3][i];
+    double a = 0.0;
+#pragma unroll
+    for (int w = 0; w < kQprepWaves; ++w) a += red[w][threadIdx.x];
+    gpart[((int64_t)tile * Hkv + h) * D + threadIdx.x] = a;
   }
 }
 
 // ---------------------------------------------------------------------------
-// K1b: mean query M of (sequence, KV head) from the tile sums (fixed order,
-// fp64), then c_t = cos(M, g_t) for the tile's tokens.
+// K1b: mean query M of (sequence, KV head) from the tile sums (fp64, fixed
+// summation order), then c_t = cos(M, g_t) for the tile's tokens in fp64.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void qprep_cos_kernel(
+__global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TC, const float* __restrict__ g, const double* __restrict__ gpart,
     float* __restrict__ qcos) {
+  constexpr int P = kQprepThreads / D;  // partial sums per channel
   const int tile = blockIdx.x, h = blockIdx.y;
   const int32_t* qt_off = plan;
   const int s = upper_seq(qt_off, S, tile);
-  const int t0 = (tile - qt_off[s]) * kQprepTokens;
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
+  __shared__ double parts[P][D];
   __shared__ double Md[D];
-  __shared__ double red[4];
+  __shared__ double red[kQprepWaves];
+  {
+    const int d = threadIdx.x % D, p = threadIdx.x / D;
+    const int k0 = qt_off[s], k1 = qt_off[s + 1];
+    double a = 0.0;
+    for (int k = k0 + p; k < k1; k += 4 * P) {
+      double v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = k + u * P;
+        v[u] = kk < k1 ? gpart[((int64_t)kk * Hkv + h) * D + d] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a += v[u];
+    }
+    parts[p][d] = a;
+  }
+  __syncthreads();
   double sq = 0.0;
   if (threadIdx.x < D) {
-    double acc = 0.0;
-    for (int k = qt_off[s]; k < qt_off[s + 1]; ++k)
-      acc += gpart[((int64_t)k * Hkv + h) * D + threadIdx.x];
-    acc /= (double)C;
-    Md[threadIdx.x] = acc;
-    sq = acc * acc;
+    double a = 0.0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) a += parts[p][threadIdx.x];
+    a /= (double)C;
+    Md[threadIdx.x] = a;
+    sq = a * a;
   }
   sq = wave_sum(sq);
   if (lane == 0) red[wave] = sq;
   __syncthreads();
-  const double mnorm = sqrt(red[0] + red[1] + red[2] + red[3]);
+  double msq = 0.0;
+#pragma unroll
+  for (int w = 0; w < kQprepWaves; ++w) msq += red[w];
+  const double mnorm = sqrt(msq);
 
   constexpr int EPL = D / 64;
   double m[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) m[e] = Md[lane * EPL + e];
-  for (int i = 0; i < kQprepTokens / 4; ++i) {
-    const int t = t0 + wave * (kQprepTokens / 4) + i;
-    if (t >= C) break;
-    const float* gr = g + ((int64_t)(c_off + t) * Hkv + h) * D + lane * EPL;
+  const int tw = (tile - qt_off[s]) * kQprepTokens + wave * kTokPerWave;
+  float x[kTokPerWave][EPL];
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i) {
+    const int t = tw + i;
+    const float* gr = g + ((int64_t)(c_off + (t < C ? t : 0)) * Hkv + h) * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[i][e] = gr[e];
+  }
+#pragma unroll
+  for (int i = 0; i < kTokPerWave; ++i) {
     double dot = 0.0, gg = 0.0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      const double x = (double)gr[e];
-      dot += x * m[e];
-      gg += x * x;
+      const double v = (double)x[i][e];
+      dot += v * m[e];
+      gg += v * v;
     }
     dot = wave_sum(dot);
     gg = wave_sum(gg);
-    if (lane == 0) {
+    const int t = tw + i;
+    if (lane == 0 && t < C) {
       const double den = mnorm * sqrt(gg);
       qcos[(int64_t)h * TC + c_off + t] = den > 0.0 ? (float)(dot / den) : 0.f;
     }
@@ -188,11 +231,12 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
                         float* qcos, hipStream_t st) {
   if (p.NQT == 0) return hipSuccess;
   dim3 grid((unsigned)p.NQT, (unsigned)p.Hkv);
+  const dim3 block(kQprepThreads);
   const int32_t* plan = (const int32_t*)(ws + w.plan);
   float* g = (float*)(ws + w.g);
   double* gpart = (double*)(ws + w.gpart);
 #define QUOKA_QPREP(T, D)                                                                    \
-  hipLaunchKernelGGL((qprep_g_kernel<T, D>), grid, dim3(256), 0, st, (const T*)q, p.cu_chunk, \
+  hipLaunchKernelGGL((qprep_g_kernel<T, D>), grid, block, 0, st, (const T*)q, p.cu_chunk, \
                      plan, p.S, p.Hq, p.Hkv, p.G, g, gpart)
   if (p.dtype == QUOKA_BF16) {
     if (p.D == 128) QUOKA_QPREP(bf16, 128); else QUOKA_QPREP(bf16, 64);
@@ -203,10 +247,10 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.D == 128)
-    hipLaunchKernelGGL((qprep_cos_kernel<128>), grid, dim3(256), 0, st, p.cu_chunk, plan, p.S,
+    hipLaunchKernelGGL((qprep_cos_kernel<128>), grid, block, 0, st, p.cu_chunk, plan, p.S,
                        p.Hkv, p.TC, g, gpart, qcos);
   else
-    hipLaunchKernelGGL((qprep_cos_kernel<64>), grid, dim3(256), 0, st, p.cu_chunk, plan, p.S,
+    hipLaunchKernelGGL((qprep_cos_kernel<64>), grid, block, 0, st, p.cu_chunk, plan, p.S,
                        p.Hkv, p.TC, g, gpart, qcos);
   return hipGetLastError();
 }
@@ -245,17 +289,17 @@ __global__ __launch_bounds__(256) void qselect_kernel(
   auto key_of = [&](int t) -> uint64_t {
     return ((uint64_t)float_order_key(src[t]) << 32) | (uint32_t)t;
   };
-  uint64_t thr = ~0ull;
-  if (n < C) thr = radix_select_kth<false>(key_of, C, n, rs);  // n-th smallest key
+  uint64_t prefix = ~0ull, mask = ~0ull;  // keep everything when n == C
+  if (n < C) radix_select<false>(key_of, C, n, rs, prefix, mask);
 
   // ascending compaction of the kept tokens
   const int per = (C + blockDim.x - 1) / blockDim.x;
   const int b0 = threadIdx.x * per, b1 = min(C, b0 + per);
   int cnt = 0;
-  for (int t = b0; t < b1; ++t) cnt += (key_of(t) <= thr);
+  for (int t = b0; t < b1; ++t) cnt += radix_taken<false>(key_of(t), prefix, mask);
   int pos = block_exclusive_scan_256(cnt, rs);
   for (int t = b0; t < b1; ++t) {
-    if (key_of(t) <= thr) {
+    if (radix_taken<false>(key_of(t), prefix, mask)) {
       out[pos] = t;
       kept[pos] = t;
       ++pos;
@@ -268,22 +312,30 @@ __global__ __launch_bounds__(256) void qselect_kernel(
   // kept group queries for the scorer
   if constexpr (kMfma) {
     // A operand of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and the
-    // 8 d-values (l/16)*8.. of the 32-wide d-step. Rows past n repeat row 0,
+    // 8 d-values (l/16)*8.. of the 32-wide d-step; layout
+    // [qb][ds][term: hi, lo][lane] of bf16x8. Rows past n repeat row 0,
     // which leaves the max over kept tokens unchanged.
-    bf16* dst = (bf16*)gsel + (int64_t)prob * nq_pad * D * 2;
-    const int total = nq_pad * D * 2;
-    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-      const int e = idx & 7;
-      const int lane = (idx >> 3) & 63;
-      const int term = (idx >> 9) & 1;
-      const int rest = idx >> 10;  // qb * (D/32) + ds
-      const int ds = rest % (D / 32), qb = rest / (D / 32);
+    constexpr int NDS = D / 32;
+    bf16x8* dst = (bf16x8*)gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64;
+    const int total = (nq_pad / 16) * NDS * 64;
+    for (int v = threadIdx.x; v < total; v += blockDim.x) {
+      const int lane = v & 63;
+      const int rest = v >> 6;  // qb * NDS + ds
+      const int ds = rest % NDS, qb = rest / NDS;
       const int row = qb * 16 + (lane & 15);
-      const int d = ds * 32 + (lane >> 4) * 8 + e;
+      const int d0 = ds * 32 + (lane >> 4) * 8;
       const int t = kept[row < n ? row : 0];
-      const float x = g[((int64_t)(c_off + t) * Hkv + h) * D + d];
-      const bf16 hi = (bf16)x;
-      dst[idx] = term == 0 ? hi : (bf16)(x - (float)hi);
+      const float4* gp = (const float4*)(g + ((int64_t)(c_off + t) * Hkv + h) * D + d0);
+      const float4 x0 = gp[0], x1 = gp[1];
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = (bf16)x[e];
+        lo[e] = (bf16)(x[e] - (float)hi[e]);
+      }
+      dst[(rest * 2 + 0) * 64 + lane] = hi;
+      dst[(rest * 2 + 1) * 64 + lane] = lo;
     }
   } else {
     float* dst = (float*)gsel + (int64_t)prob * nq_pad * D;

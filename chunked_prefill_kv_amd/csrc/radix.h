@@ -9,8 +9,10 @@ namespace quoka {
 struct RadixScratch {
   uint32_t hist[256];
   uint32_t wsum[4];
+  uint64_t wand[4], wor[4];
   uint32_t digit;
   uint32_t rem;
+  uint32_t done;
 };
 
 // Inclusive prefix sum of one value per thread over a 256-thread block.
@@ -45,15 +47,46 @@ __device__ __forceinline__ uint32_t block_sum_256(uint32_t v, RadixScratch& rs) 
   return t;
 }
 
-// The k-th smallest (kLargest = false) or k-th largest (kLargest = true) of N
-// unique 64-bit keys key_of(0..N-1), 1 <= k <= N. Eight passes of 8-bit
-// digits from the top; each pass histograms the keys that still match the
-// digits fixed so far. Exact: the result is a key that occurs in the input.
+// Exact selection of the k smallest (kLargest = false) or k largest
+// (kLargest = true) of N unique 64-bit keys key_of(0..N-1), 1 <= k < N.
+// Result: the selected keys are exactly those with
+//     (key & mask) <= prefix   (smallest)   or   (key & mask) >= prefix (largest).
+// The bits all keys share are skipped first; then 8-bit digits are resolved
+// from the top, histogramming the keys that still match, until the bucket at
+// the boundary is taken whole (or every digit is fixed, when prefix is the
+// k-th key itself).
 template <bool kLargest, typename KeyFn>
-__device__ uint64_t radix_select_kth(KeyFn key_of, int N, int k, RadixScratch& rs) {
-  uint64_t prefix = 0, mask = 0;
+__device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch& rs, uint64_t& prefix,
+                             uint64_t& mask) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint64_t a = ~0ull, o = 0ull;
+  for (int i = threadIdx.x; i < N; i += 256) {
+    const uint64_t key = key_of(i);
+    a &= key;
+    o |= key;
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    a &= __shfl_xor(a, s, 64);
+    o |= __shfl_xor(o, s, 64);
+  }
+  if (lane == 0) { rs.wand[w] = a; rs.wor[w] = o; }
+  __syncthreads();
+  a = rs.wand[0] & rs.wand[1] & rs.wand[2] & rs.wand[3];
+  o = rs.wor[0] | rs.wor[1] | rs.wor[2] | rs.wor[3];
+  __syncthreads();
+  const uint64_t diff = a ^ o;
+  if (diff == 0ull) {  // a single distinct key
+    prefix = a;
+    mask = ~0ull;
+    return;
+  }
+  const int top = 63 - __clzll(diff);
+  const int shift0 = (top / 8) * 8;
+  mask = shift0 + 8 >= 64 ? 0ull : (~0ull << (shift0 + 8));
+  prefix = a & mask;
   uint32_t rem = (uint32_t)k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int shift = shift0; shift >= 0; shift -= 8) {
     rs.hist[threadIdx.x] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < N; i += 256) {
@@ -71,16 +104,23 @@ __device__ uint64_t radix_select_kth(KeyFn key_of, int N, int k, RadixScratch& r
     if (v > 0 && excl < rem && rem <= incl) {
       rs.digit = threadIdx.x;
       rs.rem = rem - excl;
+      rs.done = incl == rem;
     }
     __syncthreads();
     uint32_t d = rs.digit;
     rem = rs.rem;
+    const bool done = rs.done != 0u;
     if (kLargest) d = 255u - d;
     prefix |= (uint64_t)d << shift;
     mask |= 255ull << shift;
     __syncthreads();
+    if (done) break;
   }
-  return prefix;
+}
+
+template <bool kLargest>
+__device__ __forceinline__ bool radix_taken(uint64_t key, uint64_t prefix, uint64_t mask) {
+  return kLargest ? (key & mask) >= prefix : (key & mask) <= prefix;
 }
 
 }  // namespace quoka

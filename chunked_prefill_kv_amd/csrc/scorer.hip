@@ -22,7 +22,8 @@ namespace quoka {
 //   C = [16 queries x 16 keys]; lane l holds key column l%16, so the max over
 //       queries is a per-lane max followed by two cross-lane steps.
 // One workgroup = 4 waves = up to kScoreKeys keys of one (sequence, KV head);
-// each wave takes 64 keys (4 blocks of 16) per iteration.
+// each wave takes 64 keys (4 blocks of 16) per iteration, and loads the keys
+// of all its iterations before the first MFMA.
 template <int D>
 __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     const bf16* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
@@ -53,28 +54,38 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;
-  for (int it = 0; it < kScoreKeys / 256; ++it) {
+  constexpr int NIT = kScoreKeys / 256;  // 64-key iterations per wave
+  // every key load of the wave is issued before the first MFMA
+  bf16x8 b[NIT][4][NDS];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = k_begin + it * 256 + wave * 64 + kb * 16 + (lane & 15);
+      const bool ok = key < k_end;
+      const bf16* row =
+          k_hist + ((int64_t)(h_off + (ok ? key : 0)) * Hkv + h) * D + (lane >> 4) * 8;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 v = *(const bf16x8*)(row + ds * 32);
+        b[it][kb][ds] = ok ? v : (bf16x8){};
+      }
+    }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
     const int k0 = k_begin + it * 256 + wave * 64;
     if (k0 >= k_end) break;
-    bf16x8 b[4][NDS];
     float nsq[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int key = k0 + kb * 16 + (lane & 15);
-      const bool ok = key < k_end;
-      const bf16* row = k_hist + ((int64_t)(h_off + (ok ? key : 0)) * Hkv + h) * D + (lane >> 4) * 8;
       float ss = 0.f;
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        bf16x8 v = *(const bf16x8*)(row + ds * 32);
-        if (!ok) v = (bf16x8){};
-        b[kb][ds] = v;
+      for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = (float)v[e];
+          const float x = (float)b[it][kb][ds][e];
           ss = fmaf(x, x, ss);
         }
-      }
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
       nsq[kb] = ss;
@@ -90,10 +101,10 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
         const bf16x8 alo = lg[((qb * NDS + ds) * 2 + 1) * 64 + lane];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b[kb][ds], acc[kb], 0, 0, 0);
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b[it][kb][ds], acc[kb], 0, 0, 0);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b[kb][ds], acc[kb], 0, 0, 0);
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b[it][kb][ds], acc[kb], 0, 0, 0);
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)

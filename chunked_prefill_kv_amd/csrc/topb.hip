@@ -75,19 +75,27 @@ __global__ __launch_bounds__(256) void topb_filter_kernel(
   find_threshold_bin(hist + (int64_t)prob * kScoreBins, L, B_eff, rs, &bstar, &above, &need);
   if (lt == 0 && threadIdx.x == 0) {
     Threshold t;
-    t.bstar = bstar; t.above = above; t.need = need; t.pad = 0; t.t64 = ~0ull;
+    t.bstar = bstar; t.above = above; t.need = need; t.pad = 0;
+    t.prefix = ~0ull; t.mask = ~0ull;
     thr[prob] = t;
   }
   const float* srow = scores + (int64_t)h * TL + h_off;
   uint64_t* crow = cand + (int64_t)h * TL + h_off;
   const int lane = threadIdx.x & 63;
   const int k0 = lt * kTopbKeys;
+  constexpr int PER = kTopbKeys / 256;
+  float sc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int key = k0 + i * 256 + threadIdx.x;
+    sc[i] = key < L ? srow[key] : 0.f;
+  }
   uint32_t gt = 0;
-  for (int i = 0; i < kTopbKeys / 256; ++i) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
     const int key = k0 + i * 256 + threadIdx.x;
     const bool ok = key < L;
-    const float sc = ok ? srow[key] : 0.f;
-    const int bin = score_bin(sc);
+    const int bin = score_bin(sc[i]);
     gt += (ok && bin > bstar);
     const bool isc = ok && bin == bstar;
     const uint64_t bal = __ballot(isc);
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(256) void topb_filter_kernel(
       base = __shfl(base, 0, 64);
       if (isc) {
         const uint32_t rank = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        crow[base + rank] = cand_key(sc, key);
+        crow[base + rank] = cand_key(sc[i], key);
       }
     }
   }
@@ -129,13 +137,18 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(
     src = lc;
   }
   __syncthreads();
-  const uint64_t t64 = radix_select_kth<true>([&](int i) { return src[i]; }, n, t.need, rs);
-  if (threadIdx.x == 0) thr[prob].t64 = t64;
+  uint64_t prefix = ~0ull, mask = 0ull;  // n == need: every candidate is chosen
+  if (t.need < n) radix_select<true>([&](int i) { return src[i]; }, n, t.need, rs, prefix, mask);
+  else prefix = 0ull;
+  if (threadIdx.x == 0) {
+    thr[prob].prefix = prefix;
+    thr[prob].mask = mask;
+  }
   const int32_t* kt_off = plan + 2 * (S + 1);
   uint32_t* ch = chcount + (int64_t)h * NKT + kt_off[s];
   for (int i = threadIdx.x; i < n; i += 256) {
     const uint64_t c = src[i];
-    if (c >= t64) {
+    if (radix_taken<true>(c, prefix, mask)) {
       const int key = (int)(0xFFFFFFFFu - (uint32_t)c);
       atomicAdd(&ch[key / kTopbKeys], 1u);
     }
@@ -172,7 +185,8 @@ __global__ __launch_bounds__(256) void topb_write_kernel(
     if (key < L) {
       const float sc = srow[key];
       const int bin = score_bin(sc);
-      const bool sel = bin > t.bstar || (bin == t.bstar && cand_key(sc, key) >= t.t64);
+      const bool sel = bin > t.bstar ||
+                       (bin == t.bstar && radix_taken<true>(cand_key(sc, key), t.prefix, t.mask));
       flags |= (uint32_t)sel << e;
       cnt += sel;
     }
