@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--config", default="llama8b", choices=sorted(DESCR))
     ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times) and exit: the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is built "
@@ -104,6 +107,16 @@ def main():
     import torch
     import chunked_prefill_kv_amd as cpk
     from workloads import make_config
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
 
     w = make_config(args.config)
     dev = torch.device("cuda", 0)

@@ -121,6 +121,12 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
   if (p->TC * p->Hq > INT32_MAX || p->TL * p->Hkv > INT32_MAX)
     return fail(QUOKA_EUNSUPPORTED, "token totals too large");
   if ((int64_t)p->maxC * p->G > INT32_MAX) return fail(QUOKA_EUNSUPPORTED, "chunk too long");
+  // kernels address one sequence's rows through 32-bit buffer offsets
+  const int64_t elem = sh->dtype == QUOKA_BF16 ? 2 : 4;
+  const int64_t row = (int64_t)p->Hkv * p->D * elem;
+  if ((int64_t)p->maxL * row > INT32_MAX || (int64_t)p->maxC * row > INT32_MAX ||
+      (int64_t)kv_budget * p->D * elem > INT32_MAX)
+    return fail(QUOKA_EUNSUPPORTED, "a sequence's K/V rows exceed 2 GiB");
   p->q_budget = q_budget;
   p->kv_budget = kv_budget;
   p->nq_pad = (q_budget + 15) / 16 * 16;

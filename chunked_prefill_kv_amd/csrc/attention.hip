@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 // share the KV head share every K/V tile. Each wave owns 32 rows.
 //   S^T = K Q^T  : A = K tile rows from LDS, B = the wave's Q held in VGPRs,
 //                  C lane l = query column l%32, 16 key rows.
-//   O^T += V^T P^T: A = V^T from LDS (stored transposed), B = P taken straight
+//   O^T += V^T P^T: A = V^T via LDS transpose reads of row-major V, B = P taken straight
 //                  from the S^T accumulators; the 16 keys of a k-step are the
 //                  ones the lane already holds, so P never leaves registers.
 // K/V tiles of 64 keys: first the kept history (masked past B_eff), then the
@@ -116,62 +116,57 @@ template <int D>
 struct AttnTile {
   static constexpr int KT = 64;                  // keys per tile
   static constexpr int KSTR = D + 8;             // K row stride in LDS (elements)
-  static constexpr int VSTR = KT + 8;            // V^T row stride in LDS (elements)
-  static constexpr int KCH = KT * D / 8 / 256;   // 16-byte K chunks per thread
-  static constexpr int KPT = D / 32;             // V keys per thread (x 8 d-values)
+  static constexpr int VSTR = D + 32;            // V row stride in LDS (elements)
+  static constexpr int NCH = KT * D / 8 / 256;   // 16-byte chunks per thread, K and V each
   static constexpr int K_ELEMS = KT * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
+  static constexpr int V_ELEMS = KT * VSTR;
 };
 
+// Global -> registers: thread takes 16-byte chunks c = tid + 256 i of the
+// 64 x D tile (row c / (D/8)). The buffer resources start at the tile's first
+// row and end at the last valid row, so rows past the end read as zeros
+// without any per-element select.
 template <int D>
-__device__ __forceinline__ void attn_load_tile(const bf16* __restrict__ kp,
-                                               const bf16* __restrict__ vp, int64_t rstride,
-                                               int kbase, int klim, bf16x8 (&kr)[AttnTile<D>::KCH],
-                                               bf16x8 (&vr)[AttnTile<D>::KPT]) {
+__device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                               uint32_t row_bytes,
+                                               bf16x8 (&kr)[AttnTile<D>::NCH],
+                                               bf16x8 (&vr)[AttnTile<D>::NCH]) {
   using TT = AttnTile<D>;
 #pragma unroll
-  for (int i = 0; i < TT::KCH; ++i) {
+  for (int i = 0; i < TT::NCH; ++i) {
     const int c = threadIdx.x + 256 * i;
-    const int row = c / (D / 8), part = c % (D / 8);
-    const int key = kbase + row;
-    const bf16x8 v = *(const bf16x8*)(kp + (int64_t)(key < klim ? key : 0) * rstride + part * 8);
-    kr[i] = key < klim ? v : (bf16x8){};
-  }
-  const int dg = threadIdx.x % (D / 8), kq = threadIdx.x / (D / 8);
-#pragma unroll
-  for (int i = 0; i < TT::KPT; ++i) {
-    const int key = kbase + kq * TT::KPT + i;
-    const bf16x8 v = *(const bf16x8*)(vp + (int64_t)(key < klim ? key : 0) * rstride + dg * 8);
-    vr[i] = key < klim ? v : (bf16x8){};
+    const uint32_t off = (uint32_t)(c / (D / 8)) * row_bytes + (uint32_t)(c % (D / 8)) * 16u;
+    kr[i] = buffer_load_bf16x8(rk, off);
+    vr[i] = buffer_load_bf16x8(rv, off);
   }
 }
 
+// Registers -> LDS, both row-major (key, d). V is transposed later by the
+// LDS transpose read that feeds the P.V MFMA.
 template <int D>
-__device__ __forceinline__ void attn_store_tile(bf16* __restrict__ Ks, bf16* __restrict__ Vt,
-                                                const bf16x8 (&kr)[AttnTile<D>::KCH],
-                                                const bf16x8 (&vr)[AttnTile<D>::KPT]) {
+__device__ __forceinline__ void attn_store_tile(bf16* __restrict__ Ks, bf16* __restrict__ Vs,
+                                                const bf16x8 (&kr)[AttnTile<D>::NCH],
+                                                const bf16x8 (&vr)[AttnTile<D>::NCH]) {
   using TT = AttnTile<D>;
 #pragma unroll
-  for (int i = 0; i < TT::KCH; ++i) {
+  for (int i = 0; i < TT::NCH; ++i) {
     const int c = threadIdx.x + 256 * i;
     const int row = c / (D / 8), part = c % (D / 8);
     *(bf16x8*)&Ks[row * TT::KSTR + part * 8] = kr[i];
+    *(bf16x8*)&Vs[row * TT::VSTR + part * 8] = vr[i];
   }
-  // V^T: this thread holds KPT consecutive keys x 8 consecutive d-values;
-  // each d-row gets its KPT keys in one store.
-  const int dg = threadIdx.x % (D / 8), kq = threadIdx.x / (D / 8);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bf16* dst = &Vt[(dg * 8 + e) * TT::VSTR + kq * TT::KPT];
-    if constexpr (TT::KPT == 4) {
-      bf16x4 t = {vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
-      *(bf16x4*)dst = t;
-    } else {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      bf16x2 t = {vr[0][e], vr[1][e]};
-      *(bf16x2*)dst = t;
-    }
-  }
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 4-element reads of group lanes i/4, i/4+4, i/4+8, i/4+12. With group
+// lane j pointing at V[k0 + j/4][d0 + 4 (j%4)], lane i gets V[k0 .. k0+3][d0 + i]:
+// four consecutive keys of one d, the A-operand slice of V^T.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 template <int D>
@@ -183,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   using TT = AttnTile<D>;
   constexpr int KT = TT::KT, NDS = D / 16, NDB = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][TT::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][TT::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][TT::V_ELEMS];
 
   // XCD-aware renumbering: linear block L runs on XCD L % 8; give XCD x a
   // contiguous range of logical ids (tile-fastest, then head, then sequence).
@@ -204,7 +199,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   const int h_off = cu_hist[s];
   const int Lh = cu_hist[s + 1] - h_off;
   const int B_eff = min(kv_budget, Lh);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int col = lane & 31, hi = lane >> 5;
   const int r = tile * kAttnRows + wave * 32 + col;
   const bool rvalid = r < rows;
@@ -234,93 +230,122 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   const bf16* v2 = v_chunk + ((int64_t)c_off * Hkv + h) * D;
   const int n1 = (B_eff + KT - 1) / KT;
   const int n_all = n1 + (t_last + KT) / KT;
+  const uint32_t rb1 = D * 2u, rb2 = (uint32_t)Hkv * D * 2u;            // row bytes
+  const uint32_t end1 = (uint32_t)B_eff * rb1;                           // valid bytes
+  const uint32_t end2 = (uint32_t)t_last * rb2 + D * 2u;
 
-  bf16x8 kr[TT::KCH], vr[TT::KPT];
+  bf16x8 kr[TT::NCH], vr[TT::NCH];
   auto load = [&](int it) {
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
-    attn_load_tile<D>(ph1 ? k1 : k2, ph1 ? v1 : v2, ph1 ? (int64_t)D : (int64_t)Hkv * D, kbase,
-                      ph1 ? B_eff : t_last + 1, kr, vr);
+    const uint32_t rb = ph1 ? rb1 : rb2;
+    const uint32_t skip = (uint32_t)kbase * rb;
+    const uint32_t left = (ph1 ? end1 : end2) - skip;
+    const bf16* kp = (ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2);
+    const bf16* vp = (ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2);
+    attn_load_tile<D>(make_rsrc(kp, left), make_rsrc(vp, left), rb, kr, vr);
   };
   load(0);
-  attn_store_tile<D>(Ks[0], Vt[0], kr, vr);
+  attn_store_tile<D>(Ks[0], Vs[0], kr, vr);
   __syncthreads();
+
+  // lane-constant parts of the LDS read addresses
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int k_rd = col * TT::KSTR + hi * 8;                                  // K rows for S^T
+  const int v_rd = (hi * 4 + (j16 >> 2)) * TT::VSTR + (g16 & 1) * 16 + 4 * (j16 & 3);
 
   for (int it = 0; it < n_all; ++it) {
     const int buf = it & 1;
     if (it + 1 < n_all) load(it + 1);
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
-    const bf16* ks = Ks[buf];
-    const bf16* vt = Vt[buf];
+    const bf16* ks = Ks[buf] + k_rd;
+    const bf16* vs = Vs[buf] + v_rd;
 
-    f32x16 sacc[2];
+    __builtin_amdgcn_s_setprio(1);
+    // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks, interleaved)
+    f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+    bf16x8 ka[2][NDS];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      sacc[sb] = (f32x16){};
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8 a = *(const bf16x8*)&ks[(sb * 32 + col) * TT::KSTR + ds * 16 + hi * 8];
-        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], sacc[sb], 0, 0, 0);
-      }
-    }
+      for (int ds = 0; ds < NDS; ++ds) ka[sb][ds] = *(const bf16x8*)(ks + sb * 32 * TT::KSTR + ds * 16);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[sb][ds], qreg[ds], sacc[sb], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    __builtin_amdgcn_s_setprio(0);
     // masks: history tail past B_eff; causal on tiles reaching past the
     // wave's first token
     const bool need_mask = ph1 ? (kbase + KT > B_eff) : (kbase + KT - 1 > t_wave_first);
     if (need_mask) {
-      const int lim = ph1 ? B_eff - 1 : t;  // visible keys: key <= lim
+      const int lim = (ph1 ? B_eff - 1 : t) - kbase - hi * 4;  // visible: key offset <= lim
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int key = kbase + sb * 32 + hi * 4 + jj + 8 * i;
-            if (key > lim) sacc[sb][i * 4 + jj] = -INFINITY;
-          }
+          for (int jj = 0; jj < 4; ++jj)
+            if (sb * 32 + jj + 8 * i > lim) sacc[sb][i * 4 + jj] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_new > m_run ? exp2f((m_run - m_new) * scale_log2) : 1.f;
-    const float base = m_new == -INFINITY ? 0.f : m_new * scale_log2;
+    { const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+      mx = fmaxf(mx, fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1]))); }
+    // lazy rescaling: the reference max moves only when the tile's max
+    // exceeds it by more than 2^8 in the exponent, so p <= 256 and the output
+    // is rescaled on few tiles (exact either way)
+    const float m_cand = fmaxf(m_run, mx);
+    const bool upd = (m_cand - m_run) * scale_log2 > 8.0f;
+    if (__ballot(upd)) {
+      const float m_new = upd ? m_cand : m_run;
+      const float alpha = upd ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float base = m_run * scale_log2;
     bf16x8 pb[2][2];
-    float ps = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float p = exp2f(fmaf(sacc[sb][i * 4 + jj], scale_log2, -base));
-          ps += p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sb][i * 4 + jj], scale_log2, -base));
+          l_part += p;
           pb[sb][i >> 1][(i & 1) * 4 + jj] = (bf16)p;
         }
-    l_part = fmaf(l_part, alpha, ps);
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
+    __builtin_amdgcn_s_setprio(1);
+    // O^T += V^T P^T; the A operand is read transposed from row-major V: lane
+    // group g = lane/16 covers d0 = db*32 + (g&1)*16, keys kb0 = ... + hi*4
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-    }
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const bf16* vrow = vt + (db * 32 + col) * TT::VSTR;
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 a[NDB];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int kb0 = sb * 32 + kk * 16 + hi * 4;
-          const bf16x4 lo4 = *(const bf16x4*)(vrow + kb0);
-          const bf16x4 hi4 = *(const bf16x4*)(vrow + kb0 + 8);
-          const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[sb][kk], oacc[db], 0, 0, 0);
+        for (int db = 0; db < NDB; ++db) {
+          const bf16* p0 = vs + (sb * 32 + kk * 16) * TT::VSTR + db * 32;
+          const bf16x4 lo4 = lds_read_tr16(p0);
+          const bf16x4 hi4 = lds_read_tr16(p0 + 8 * TT::VSTR);
+          a[db] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-    }
-    if (it + 1 < n_all) attn_store_tile<D>(Ks[buf ^ 1], Vt[buf ^ 1], kr, vr);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pb[sb][kk], oacc[db], 0, 0, 0);
+      }
+    __builtin_amdgcn_s_setprio(0);
+    if (it + 1 < n_all) attn_store_tile<D>(Ks[buf ^ 1], Vs[buf ^ 1], kr, vr);
     __syncthreads();
   }
 

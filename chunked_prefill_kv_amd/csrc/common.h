@@ -63,6 +63,46 @@ __device__ __forceinline__ int score_bin(float s) {
   return (int)x;
 }
 
+// ---- buffer loads ----------------------------------------------------------
+// Raw buffer resource over [p, p + nbytes): loads at byte offsets >= nbytes
+// return zeros (bounds checked in hardware on the VGPR offset). p and nbytes
+// must be the same in every lane of the wave; they are moved to scalar
+// registers explicitly (values the compiler computed in VGPRs, such as
+// integer quotients, would otherwise be legalised with a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* pu = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, (int)__builtin_amdgcn_readfirstlane(nbytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ bf16x8 buffer_load_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- block-wide copies ------------------------------------------------------
+// dst[i] = src[i] for i < n by a block of NT threads, with up to U loads per
+// thread in flight before their stores (a plain strided loop waits for each
+// load in turn).
+template <int NT, int U, typename T>
+__device__ __forceinline__ void block_copy(T* __restrict__ dst, const T* __restrict__ src, int n) {
+  for (int base = 0; base < n; base += NT * U) {
+    T v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * NT + (int)threadIdx.x;
+      if (i < n) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * NT + (int)threadIdx.x;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+}
+
 // Largest s in [0, n) with off[s] <= v, for non-decreasing off[0..n].
 __device__ __forceinline__ int upper_seq(const int32_t* off, int n, int v) {
   int lo = 0, hi = n - 1;

@@ -12,7 +12,7 @@ namespace quoka {
 
 // Tilings (all per sequence; tiles never straddle two sequences).
 constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
-constexpr int kScoreKeys = 512;      // history keys per scorer workgroup
+constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup
 constexpr int kTopbKeys = 512;       // history keys per top-B workgroup
 constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
 

@@ -60,6 +60,29 @@ constexpr int kQprepThreads = 1024;
 constexpr int kQprepWaves = kQprepThreads / 64;
 constexpr int kTokPerWave = kQprepTokens / kQprepWaves;  // 4
 
+// EPL consecutive elements as fp32, with 16-byte (or 8-byte) vector loads.
+template <typename T, int EPL>
+__device__ __forceinline__ void load_row(const T* __restrict__ p, float (&x)[EPL]) {
+  if constexpr (sizeof(T) == 2) {
+    static_assert(EPL % 4 == 0, "bf16 rows load 4 or 8 elements");
+    if constexpr (EPL == 8) {
+      const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+    } else {
+      const bf16x4 v = *(const bf16x4*)p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 v = *(const float4*)(p + e);
+      x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ cu_chunk,
@@ -90,8 +113,9 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
       const bool ok = t < C && j < G;
       const T* row = q + ((int64_t)(c_off + (ok ? t : 0)) * Hq + (int64_t)h * G + (ok ? j : 0)) * D +
                      sub * EPL;
+      load_row<T, EPL>(row, x[i]);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x[i][e] = ok ? to_f32(row[e]) : 0.f;
+      for (int e = 0; e < EPL; ++e) x[i][e] = ok ? x[i][e] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kTokPerWave; ++i) {
@@ -121,10 +145,10 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     if (grp == 0 && t < C) {
       float* dst = g + ((int64_t)(c_off + t) * Hkv + h) * D + sub * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        dst[e] = acc[i][e];
-        part[e] += (double)acc[i][e];
-      }
+      for (int e = 0; e < EPL; e += 4)
+        *(float4*)(dst + e) = make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part[e] += (double)acc[i][e];
     }
   }
   __shared__ double red[kQprepWaves][D];
@@ -281,7 +305,7 @@ __global__ __launch_bounds__(256) void qselect_kernel(
 
   const float* src = qcos + (int64_t)h * TC + c_off;
   if (C <= kQselCap) {
-    for (int i = threadIdx.x; i < C; i += blockDim.x) cs[i] = src[i];
+    block_copy<256, 8>(cs, src, C);
     src = cs;
   }
   __syncthreads();
@@ -318,24 +342,36 @@ __global__ __launch_bounds__(256) void qselect_kernel(
     constexpr int NDS = D / 32;
     bf16x8* dst = (bf16x8*)gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64;
     const int total = (nq_pad / 16) * NDS * 64;
-    for (int v = threadIdx.x; v < total; v += blockDim.x) {
-      const int lane = v & 63;
-      const int rest = v >> 6;  // qb * NDS + ds
-      const int ds = rest % NDS, qb = rest / NDS;
-      const int row = qb * 16 + (lane & 15);
-      const int d0 = ds * 32 + (lane >> 4) * 8;
-      const int t = kept[row < n ? row : 0];
-      const float4* gp = (const float4*)(g + ((int64_t)(c_off + t) * Hkv + h) * D + d0);
-      const float4 x0 = gp[0], x1 = gp[1];
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      bf16x8 hi, lo;
+    constexpr int U = 4;  // rows in flight per thread
+    for (int base = 0; base < total; base += 256 * U) {
+      float4 x0[U], x1[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = (bf16)x[e];
-        lo[e] = (bf16)(x[e] - (float)hi[e]);
+      for (int u = 0; u < U; ++u) {
+        const int v = base + u * 256 + (int)threadIdx.x;
+        const int lane = v & 63, rest = v >> 6;  // rest = qb * NDS + ds
+        const int row = (rest / NDS) * 16 + (lane & 15);
+        const int d0 = (rest % NDS) * 32 + (lane >> 4) * 8;
+        const int t = kept[(v < total && row < n) ? row : 0];
+        const float4* gp = (const float4*)(g + ((int64_t)(c_off + t) * Hkv + h) * D + d0);
+        x0[u] = gp[0];
+        x1[u] = gp[1];
       }
-      dst[(rest * 2 + 0) * 64 + lane] = hi;
-      dst[(rest * 2 + 1) * 64 + lane] = lo;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = base + u * 256 + (int)threadIdx.x;
+        if (v >= total) continue;
+        const int lane = v & 63, rest = v >> 6;
+        const float x[8] = {x0[u].x, x0[u].y, x0[u].z, x0[u].w,
+                            x1[u].x, x1[u].y, x1[u].z, x1[u].w};
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = (bf16)x[e];
+          lo[e] = (bf16)(x[e] - (float)hi[e]);
+        }
+        dst[(rest * 2 + 0) * 64 + lane] = hi;
+        dst[(rest * 2 + 1) * 64 + lane] = lo;
+      }
     }
   } else {
     float* dst = (float*)gsel + (int64_t)prob * nq_pad * D;

@@ -21,16 +21,19 @@ namespace quoka {
 //       contiguous bytes of one key row; 4 lanes cover 64 B of a row),
 //   C = [16 queries x 16 keys]; lane l holds key column l%16, so the max over
 //       queries is a per-lane max followed by two cross-lane steps.
-// One workgroup = 4 waves = up to kScoreKeys keys of one (sequence, KV head);
-// each wave takes 64 keys (4 blocks of 16) per iteration, and loads the keys
-// of all its iterations before the first MFMA.
+// One workgroup = 4 waves = up to kScoreKeys keys of one (sequence, KV head).
+// Each wave streams 64-key blocks (4 MFMA blocks of 16 keys): the next block
+// is in flight while the current one is scored. Keys are read through a
+// buffer resource that ends at the sequence's last key, so reads past it
+// return zeros (those keys are never written).
 template <int D>
 __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     const bf16* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int q_budget, int nq_pad, const bf16x8* __restrict__ gsel,
     float* __restrict__ scores, uint32_t* __restrict__ hist) {
-  constexpr int NDS = D / 32;  // d-steps per key
+  constexpr int NDS = D / 32;                 // d-steps per key
+  constexpr int NIT = kScoreKeys / 256;       // 64-key blocks per wave
   const int blk = blockIdx.x, h = blockIdx.y;
   const int32_t* sb_off = plan + (S + 1);
   const int s = upper_seq(sb_off, S, blk);
@@ -40,40 +43,41 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
   const int k_end = min(L, k_begin + kScoreKeys);
   const int n = min(q_budget, cu_chunk[s + 1] - cu_chunk[s]);
   const int nqb = (n + 15) / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int prob = s * Hkv + h;
+
+  // keys [0, k_end) of this (sequence, head); row stride Hkv * D
+  const uint32_t row_bytes = (uint32_t)Hkv * D * 2u;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(k_hist + ((int64_t)h_off * Hkv + h) * D, (uint32_t)(k_end - 1) * row_bytes + D * 2u);
+  const uint32_t lane_off = (uint32_t)(lane & 15) * row_bytes + (uint32_t)(lane >> 4) * 16u;
+  auto load = [&](int it, bf16x8 (&b)[4][NDS]) {
+    const uint32_t k0 = (uint32_t)(k_begin + it * 256 + wave * 64);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds)
+        b[kb][ds] = buffer_load_bf16x8(rk, (k0 + kb * 16) * row_bytes + lane_off + ds * 64u);
+  };
+  // the first key block is requested before the kept queries are staged
+  bf16x8 b0[4][NDS], b1[4][NDS];
+  if (k_begin + wave * 64 < k_end) load(0, b0);
 
   extern __shared__ char smem[];
   uint32_t* lhist = (uint32_t*)smem;                       // kScoreBins
   bf16x8* lg = (bf16x8*)(smem + kScoreBins * 4);           // nqb * NDS * 2 * 64
   for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
-  {
-    const bf16x8* src = gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64;
-    for (int i = threadIdx.x; i < nqb * NDS * 2 * 64; i += 256) lg[i] = src[i];
-  }
+  block_copy<256, 8>(lg, gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64, nqb * NDS * 2 * 64);
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;
-  constexpr int NIT = kScoreKeys / 256;  // 64-key iterations per wave
-  // every key load of the wave is issued before the first MFMA
-  bf16x8 b[NIT][4][NDS];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = k_begin + it * 256 + wave * 64 + kb * 16 + (lane & 15);
-      const bool ok = key < k_end;
-      const bf16* row =
-          k_hist + ((int64_t)(h_off + (ok ? key : 0)) * Hkv + h) * D + (lane >> 4) * 8;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8 v = *(const bf16x8*)(row + ds * 32);
-        b[it][kb][ds] = ok ? v : (bf16x8){};
-      }
-    }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
+    bf16x8 (&cur)[4][NDS] = (it & 1) ? b1 : b0;
+    bf16x8 (&nxt)[4][NDS] = (it & 1) ? b0 : b1;
     const int k0 = k_begin + it * 256 + wave * 64;
+    if (it + 1 < NIT && k0 + 256 < k_end) load(it + 1, nxt);
     if (k0 >= k_end) break;
     float nsq[4];
 #pragma unroll
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
       for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = (float)b[it][kb][ds][e];
+          const float x = (float)cur[kb][ds][e];
           ss = fmaf(x, x, ss);
         }
       ss += __shfl_xor(ss, 16, 64);
@@ -101,10 +105,10 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
         const bf16x8 alo = lg[((qb * NDS + ds) * 2 + 1) * 64 + lane];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b[it][kb][ds], acc[kb], 0, 0, 0);
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, cur[kb][ds], acc[kb], 0, 0, 0);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b[it][kb][ds], acc[kb], 0, 0, 0);
+          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, cur[kb][ds], acc[kb], 0, 0, 0);
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -156,8 +160,7 @@ __global__ __launch_bounds__(256) void scorer_valu_kernel(
   uint32_t* lhist = (uint32_t*)smem;
   float* lg = (float*)(smem + kScoreBins * 4);  // n x D
   for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
-  const float* src = gsel + (int64_t)prob * nq_pad * D;
-  for (int i = threadIdx.x; i < n * D; i += 256) lg[i] = src[i];
+  block_copy<256, 8>(lg, gsel + (int64_t)prob * nq_pad * D, n * D);
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;

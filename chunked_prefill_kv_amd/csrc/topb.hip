@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(
   const int n = (int)ccount[prob];
   const uint64_t* src = cand + (int64_t)h * TL + h_off;
   if (n <= kCandCap) {
-    for (int i = threadIdx.x; i < n; i += 256) lc[i] = src[i];
+    block_copy<256, 8>(lc, src, n);
     src = lc;
   }
   __syncthreads();
