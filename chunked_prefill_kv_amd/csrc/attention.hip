@@ -265,6 +265,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     __builtin_amdgcn_s_setprio(1);
     // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks, interleaved)
     f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+    // all 16 K operands are read before the MFMAs so LDS latency overlaps
     bf16x8 ka[2][NDS];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[sb][e]);
+    // max across the two lane halves that hold the same query column
     { const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
       mx = fmaxf(mx, fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1]))); }
     // lazy rescaling: the reference max moves only when the tile's max

@@ -166,8 +166,90 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// K1b: mean query M of (sequence, KV head) from the tile sums (fp64, fixed
-// summation order), then c_t = cos(M, g_t) for the tile's tokens in fp64.
+// K2: keep the N_q,eff tokens with the lowest cosine (ties to the lower
+// token) by an exact radix select over the unique keys
+// (order_key(c) << 32 | t), write them ascending, and lay out the kept g rows
+// for the scorer: bf16 hi/lo pairs in MFMA A-operand order, or fp32 rows.
+// ---------------------------------------------------------------------------
+constexpr int kQselCap = 12288;  // chunk tokens whose cosines are staged in LDS
+
+template <int D, bool kMfma>
+__device__ void select_kept_queries(int prob, int h, int Hkv, int c_off, int C, int q_budget,
+                                    int nq_pad, const float* __restrict__ src_g,
+                                    const float* __restrict__ g, int32_t* __restrict__ qidx,
+                                    void* __restrict__ gsel, float* cs,
+                                    RadixScratch<kQprepThreads>& rs, int32_t* kept) {
+  constexpr int NT = kQprepThreads;
+  const int n = min(q_budget, C);
+  int32_t* out = qidx + (int64_t)prob * q_budget;
+  const float* src = src_g;
+  if (C <= kQselCap) {
+    block_copy<NT, 4>(cs, src, C);
+    src = cs;
+  }
+  __syncthreads();
+  auto key_of = [&](int t) -> uint64_t {
+    return ((uint64_t)float_order_key(src[t]) << 32) | (uint32_t)t;
+  };
+  uint64_t prefix = ~0ull, mask = ~0ull;  // keep everything when n == C
+  if (n < C) radix_select<false, NT>(key_of, C, n, rs, prefix, mask);
+
+  // ascending compaction of the kept tokens
+  const int per = (C + NT - 1) / NT;
+  const int b0 = threadIdx.x * per, b1 = min(C, b0 + per);
+  uint32_t cnt = 0;
+  for (int t = b0; t < b1; ++t) cnt += radix_taken<false>(key_of(t), prefix, mask);
+  uint32_t pos = block_exclusive_scan<NT>(cnt, rs);
+  for (int t = b0; t < b1; ++t) {
+    if (radix_taken<false>(key_of(t), prefix, mask)) {
+      out[pos] = t;
+      kept[pos] = t;
+      ++pos;
+    }
+  }
+  for (int i = n + threadIdx.x; i < q_budget; i += NT) out[i] = -1;
+  if (n == 0) return;  // empty chunk: the scorer writes zero scores
+  __syncthreads();
+
+  if constexpr (kMfma) {
+    // A operand of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and the
+    // 8 d-values (l/16)*8.. of the 32-wide d-step; layout
+    // [qb][ds][term: hi, lo][lane] of bf16x8. Rows past n repeat row 0,
+    // which leaves the max over kept tokens unchanged.
+    constexpr int NDS = D / 32;
+    bf16x8* dst = (bf16x8*)gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64;
+    const int total = (nq_pad / 16) * NDS * 64;
+    for (int v = threadIdx.x; v < total; v += NT) {
+      const int lane = v & 63, rest = v >> 6;  // rest = qb * NDS + ds
+      const int row = (rest / NDS) * 16 + (lane & 15);
+      const int d0 = (rest % NDS) * 32 + (lane >> 4) * 8;
+      const int t = kept[row < n ? row : 0];
+      const float4* gp = (const float4*)(g + ((int64_t)(c_off + t) * Hkv + h) * D + d0);
+      const float4 x0 = gp[0], x1 = gp[1];
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = (bf16)x[e];
+        lo[e] = (bf16)(x[e] - (float)hi[e]);
+      }
+      dst[(rest * 2 + 0) * 64 + lane] = hi;
+      dst[(rest * 2 + 1) * 64 + lane] = lo;
+    }
+  } else {
+    float* dst = (float*)gsel + (int64_t)prob * nq_pad * D;
+    for (int idx = threadIdx.x; idx < n * D; idx += NT) {
+      const int row = idx / D, d = idx % D;
+      dst[idx] = g[((int64_t)(c_off + kept[row]) * Hkv + h) * D + d];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K1b: c_t = cos(M, g_t) for a tile of 64 tokens, fp64 dot products. Every
+// workgroup forms M = (1/C) sum_t g_t itself from the tile sums, in a fixed
+// order (a device-scope hand-off from one workgroup to the others would cost
+// an L2 write-back per workgroup on this chip, more than the repeated sum).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
@@ -186,10 +268,10 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
   __shared__ double Md[D];
   __shared__ double red[kQprepWaves];
   {
-    const int d = threadIdx.x % D, p = threadIdx.x / D;
+    const int d = threadIdx.x % D, pp = threadIdx.x / D;
     const int k0 = qt_off[s], k1 = qt_off[s + 1];
     double a = 0.0;
-    for (int k = k0 + p; k < k1; k += 4 * P) {
+    for (int k = k0 + pp; k < k1; k += 4 * P) {
       double v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -199,14 +281,14 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) a += v[u];
     }
-    parts[p][d] = a;
+    parts[pp][d] = a;
   }
   __syncthreads();
   double sq = 0.0;
   if (threadIdx.x < D) {
     double a = 0.0;
 #pragma unroll
-    for (int p = 0; p < P; ++p) a += parts[p][threadIdx.x];
+    for (int pp = 0; pp < P; ++pp) a += parts[pp][threadIdx.x];
     a /= (double)C;
     Md[threadIdx.x] = a;
     sq = a * a;
@@ -251,145 +333,62 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
   }
 }
 
+// One workgroup per (sequence, KV head): the query select, plus the -1
+// padding of sel_idx past B_eff (the top-B select writes [0, B_eff)).
+template <int D, bool kMfma>
+__global__ __launch_bounds__(kQprepThreads) void qselect_kernel(
+    const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int Hkv, int64_t TC,
+    const float* __restrict__ g, const float* __restrict__ qcos, int q_budget, int nq_pad,
+    int32_t* __restrict__ qidx, void* __restrict__ gsel, int kv_budget,
+    int32_t* __restrict__ sel_idx) {
+  const int prob = blockIdx.x, s = prob / Hkv, h = prob % Hkv;
+  const int c_off = cu_chunk[s];
+  const int C = cu_chunk[s + 1] - c_off;
+  {
+    const int L = cu_hist[s + 1] - cu_hist[s];
+    int32_t* srow = sel_idx + (int64_t)prob * kv_budget;
+    for (int i = min(kv_budget, L) + threadIdx.x; i < kv_budget; i += kQprepThreads) srow[i] = -1;
+  }
+  __shared__ float cs[kQselCap];
+  __shared__ int32_t kept[QUOKA_MAX_Q_BUDGET];
+  __shared__ RadixScratch<kQprepThreads> rs;
+  select_kept_queries<D, kMfma>(prob, h, Hkv, c_off, C, q_budget, nq_pad,
+                                qcos + (int64_t)h * TC + c_off, g, qidx, gsel, cs, rs, kept);
+}
+
 hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
-                        float* qcos, hipStream_t st) {
-  if (p.NQT == 0) return hipSuccess;
-  dim3 grid((unsigned)p.NQT, (unsigned)p.Hkv);
-  const dim3 block(kQprepThreads);
+                        float* qcos, int32_t* qidx, int32_t* sel_idx, hipStream_t st) {
   const int32_t* plan = (const int32_t*)(ws + w.plan);
   float* g = (float*)(ws + w.g);
   double* gpart = (double*)(ws + w.gpart);
-#define QUOKA_QPREP(T, D)                                                                    \
-  hipLaunchKernelGGL((qprep_g_kernel<T, D>), grid, block, 0, st, (const T*)q, p.cu_chunk, \
+  const dim3 block(kQprepThreads);
+  if (p.NQT > 0) {
+    dim3 grid((unsigned)p.NQT, (unsigned)p.Hkv);
+#define QUOKA_QPREP(T, D)                                                                     \
+  hipLaunchKernelGGL((qprep_g_kernel<T, D>), grid, block, 0, st, (const T*)q, p.cu_chunk,     \
                      plan, p.S, p.Hq, p.Hkv, p.G, g, gpart)
-  if (p.dtype == QUOKA_BF16) {
-    if (p.D == 128) QUOKA_QPREP(bf16, 128); else QUOKA_QPREP(bf16, 64);
-  } else {
-    if (p.D == 128) QUOKA_QPREP(float, 128); else QUOKA_QPREP(float, 64);
-  }
+    if (p.dtype == QUOKA_BF16) {
+      if (p.D == 128) QUOKA_QPREP(bf16, 128); else QUOKA_QPREP(bf16, 64);
+    } else {
+      if (p.D == 128) QUOKA_QPREP(float, 128); else QUOKA_QPREP(float, 64);
+    }
 #undef QUOKA_QPREP
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.D == 128)
-    hipLaunchKernelGGL((qprep_cos_kernel<128>), grid, block, 0, st, p.cu_chunk, plan, p.S,
-                       p.Hkv, p.TC, g, gpart, qcos);
-  else
-    hipLaunchKernelGGL((qprep_cos_kernel<64>), grid, block, 0, st, p.cu_chunk, plan, p.S,
-                       p.Hkv, p.TC, g, gpart, qcos);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// K2: per (sequence, KV head) keep the N_q,eff tokens with the lowest cosine
-// (ties to the lower token) by an exact radix select over the unique keys
-// (order_key(c) << 32 | t), emit them ascending, and lay out the kept g rows
-// for the scorer: bf16 hi/lo pairs in MFMA A-operand order, or fp32 rows.
-// ---------------------------------------------------------------------------
-constexpr int kQselCap = 12288;  // chunk tokens whose cosines are staged in LDS
-
-template <int D, bool kMfma>
-__global__ __launch_bounds__(256) void qselect_kernel(
-    const int32_t* __restrict__ cu_chunk, int Hkv, int64_t TC, int q_budget, int nq_pad,
-    const float* __restrict__ qcos, const float* __restrict__ g, int32_t* __restrict__ qidx,
-    void* __restrict__ gsel) {
-  const int prob = blockIdx.x;
-  const int s = prob / Hkv, h = prob % Hkv;
-  const int c_off = cu_chunk[s];
-  const int C = cu_chunk[s + 1] - c_off;
-  const int n = min(q_budget, C);
-  int32_t* out = qidx + (int64_t)prob * q_budget;
-
-  __shared__ float cs[kQselCap];
-  __shared__ int32_t kept[QUOKA_MAX_Q_BUDGET];
-  __shared__ RadixScratch rs;
-
-  const float* src = qcos + (int64_t)h * TC + c_off;
-  if (C <= kQselCap) {
-    block_copy<256, 8>(cs, src, C);
-    src = cs;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.D == 128)
+      hipLaunchKernelGGL((qprep_cos_kernel<128>), grid, block, 0, st, p.cu_chunk, plan, p.S,
+                         p.Hkv, p.TC, g, gpart, qcos);
+    else
+      hipLaunchKernelGGL((qprep_cos_kernel<64>), grid, block, 0, st, p.cu_chunk, plan, p.S,
+                         p.Hkv, p.TC, g, gpart, qcos);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  __syncthreads();
-
-  auto key_of = [&](int t) -> uint64_t {
-    return ((uint64_t)float_order_key(src[t]) << 32) | (uint32_t)t;
-  };
-  uint64_t prefix = ~0ull, mask = ~0ull;  // keep everything when n == C
-  if (n < C) radix_select<false>(key_of, C, n, rs, prefix, mask);
-
-  // ascending compaction of the kept tokens
-  const int per = (C + blockDim.x - 1) / blockDim.x;
-  const int b0 = threadIdx.x * per, b1 = min(C, b0 + per);
-  int cnt = 0;
-  for (int t = b0; t < b1; ++t) cnt += radix_taken<false>(key_of(t), prefix, mask);
-  int pos = block_exclusive_scan_256(cnt, rs);
-  for (int t = b0; t < b1; ++t) {
-    if (radix_taken<false>(key_of(t), prefix, mask)) {
-      out[pos] = t;
-      kept[pos] = t;
-      ++pos;
-    }
-  }
-  for (int i = n + threadIdx.x; i < q_budget; i += blockDim.x) out[i] = -1;
-  __syncthreads();
-  if (n == 0) return;
-
-  // kept group queries for the scorer
-  if constexpr (kMfma) {
-    // A operand of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and the
-    // 8 d-values (l/16)*8.. of the 32-wide d-step; layout
-    // [qb][ds][term: hi, lo][lane] of bf16x8. Rows past n repeat row 0,
-    // which leaves the max over kept tokens unchanged.
-    constexpr int NDS = D / 32;
-    bf16x8* dst = (bf16x8*)gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64;
-    const int total = (nq_pad / 16) * NDS * 64;
-    constexpr int U = 4;  // rows in flight per thread
-    for (int base = 0; base < total; base += 256 * U) {
-      float4 x0[U], x1[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = base + u * 256 + (int)threadIdx.x;
-        const int lane = v & 63, rest = v >> 6;  // rest = qb * NDS + ds
-        const int row = (rest / NDS) * 16 + (lane & 15);
-        const int d0 = (rest % NDS) * 32 + (lane >> 4) * 8;
-        const int t = kept[(v < total && row < n) ? row : 0];
-        const float4* gp = (const float4*)(g + ((int64_t)(c_off + t) * Hkv + h) * D + d0);
-        x0[u] = gp[0];
-        x1[u] = gp[1];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = base + u * 256 + (int)threadIdx.x;
-        if (v >= total) continue;
-        const int lane = v & 63, rest = v >> 6;
-        const float x[8] = {x0[u].x, x0[u].y, x0[u].z, x0[u].w,
-                            x1[u].x, x1[u].y, x1[u].z, x1[u].w};
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hi[e] = (bf16)x[e];
-          lo[e] = (bf16)(x[e] - (float)hi[e]);
-        }
-        dst[(rest * 2 + 0) * 64 + lane] = hi;
-        dst[(rest * 2 + 1) * 64 + lane] = lo;
-      }
-    }
-  } else {
-    float* dst = (float*)gsel + (int64_t)prob * nq_pad * D;
-    for (int idx = threadIdx.x; idx < n * D; idx += blockDim.x) {
-      const int row = idx / D, d = idx % D;
-      dst[idx] = g[((int64_t)(c_off + kept[row]) * Hkv + h) * D + d];
-    }
-  }
-}
-
-hipError_t launch_qselect(const Problem& p, char* ws, const Workspace& w, const float* qcos,
-                          int32_t* qidx, hipStream_t st) {
-  dim3 grid((unsigned)(p.S * p.Hkv));
-  const float* g = (const float*)(ws + w.g);
-  void* gsel = ws + w.gsel;
+  const dim3 sgrid((unsigned)(p.S * p.Hkv));
 #define QUOKA_QSEL(D, M)                                                                      \
-  hipLaunchKernelGGL((qselect_kernel<D, M>), grid, dim3(256), 0, st, p.cu_chunk, p.Hkv, p.TC, \
-                     p.q_budget, p.nq_pad, qcos, g, qidx, gsel)
+  hipLaunchKernelGGL((qselect_kernel<D, M>), sgrid, block, 0, st, p.cu_chunk, p.cu_hist, p.Hkv, \
+                     p.TC, g, qcos, p.q_budget, p.nq_pad, qidx, (void*)(ws + w.gsel),         \
+                     p.kv_budget, sel_idx)
   const bool mfma = p.dtype == QUOKA_BF16;
   if (p.D == 128) { if (mfma) QUOKA_QSEL(128, true); else QUOKA_QSEL(128, false); }
   else            { if (mfma) QUOKA_QSEL(64, true);  else QUOKA_QSEL(64, false); }

@@ -1,22 +1,25 @@
 // Block-wide scans and an exact radix select over unique 64-bit keys, for
-// 256-thread workgroups.
+// workgroups of NT threads (NT = 256 or 1024).
 #pragma once
 
 #include "common.h"
 
 namespace quoka {
 
+template <int NT>
 struct RadixScratch {
+  static constexpr int W = NT / 64;
   uint32_t hist[256];
-  uint32_t wsum[4];
-  uint64_t wand[4], wor[4];
+  uint32_t wsum[W];
+  uint64_t wand[W], wor[W];
   uint32_t digit;
   uint32_t rem;
   uint32_t done;
 };
 
-// Inclusive prefix sum of one value per thread over a 256-thread block.
-__device__ __forceinline__ uint32_t block_inclusive_scan_256(uint32_t v, RadixScratch& rs) {
+// Inclusive prefix sum of one value per thread over the block.
+template <int NT>
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, RadixScratch<NT>& rs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -32,17 +35,21 @@ __device__ __forceinline__ uint32_t block_inclusive_scan_256(uint32_t v, RadixSc
   return x + add;
 }
 
-__device__ __forceinline__ uint32_t block_exclusive_scan_256(uint32_t v, RadixScratch& rs) {
-  return block_inclusive_scan_256(v, rs) - v;
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, RadixScratch<NT>& rs) {
+  return block_inclusive_scan<NT>(v, rs) - v;
 }
 
-__device__ __forceinline__ uint32_t block_sum_256(uint32_t v, RadixScratch& rs) {
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, RadixScratch<NT>& rs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   if (lane == 0) rs.wsum[w] = v;
   __syncthreads();
-  const uint32_t t = rs.wsum[0] + rs.wsum[1] + rs.wsum[2] + rs.wsum[3];
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t += rs.wsum[i];
   __syncthreads();
   return t;
 }
@@ -55,12 +62,12 @@ __device__ __forceinline__ uint32_t block_sum_256(uint32_t v, RadixScratch& rs) 
 // from the top, histogramming the keys that still match, until the bucket at
 // the boundary is taken whole (or every digit is fixed, when prefix is the
 // k-th key itself).
-template <bool kLargest, typename KeyFn>
-__device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch& rs, uint64_t& prefix,
+template <bool kLargest, int NT, typename KeyFn>
+__device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch<NT>& rs, uint64_t& prefix,
                              uint64_t& mask) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint64_t a = ~0ull, o = 0ull;
-  for (int i = threadIdx.x; i < N; i += 256) {
+  for (int i = threadIdx.x; i < N; i += NT) {
     const uint64_t key = key_of(i);
     a &= key;
     o |= key;
@@ -72,8 +79,10 @@ __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch& rs, uint6
   }
   if (lane == 0) { rs.wand[w] = a; rs.wor[w] = o; }
   __syncthreads();
-  a = rs.wand[0] & rs.wand[1] & rs.wand[2] & rs.wand[3];
-  o = rs.wor[0] | rs.wor[1] | rs.wor[2] | rs.wor[3];
+  a = ~0ull;
+  o = 0ull;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) { a &= rs.wand[i]; o |= rs.wor[i]; }
   __syncthreads();
   const uint64_t diff = a ^ o;
   if (diff == 0ull) {  // a single distinct key
@@ -87,9 +96,9 @@ __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch& rs, uint6
   prefix = a & mask;
   uint32_t rem = (uint32_t)k;
   for (int shift = shift0; shift >= 0; shift -= 8) {
-    rs.hist[threadIdx.x] = 0u;
+    if (threadIdx.x < 256) rs.hist[threadIdx.x] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < N; i += 256) {
+    for (int i = threadIdx.x; i < N; i += NT) {
       const uint64_t key = key_of(i);
       if ((key & mask) == prefix) {
         uint32_t d = (uint32_t)(key >> shift) & 255u;
@@ -98,8 +107,8 @@ __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch& rs, uint6
       }
     }
     __syncthreads();
-    const uint32_t v = rs.hist[threadIdx.x];
-    const uint32_t incl = block_inclusive_scan_256(v, rs);
+    const uint32_t v = threadIdx.x < 256 ? rs.hist[threadIdx.x] : 0u;
+    const uint32_t incl = block_inclusive_scan<NT>(v, rs);
     const uint32_t excl = incl - v;
     if (v > 0 && excl < rem && rem <= incl) {
       rs.digit = threadIdx.x;
@@ -121,6 +130,42 @@ __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch& rs, uint6
 template <bool kLargest>
 __device__ __forceinline__ bool radix_taken(uint64_t key, uint64_t prefix, uint64_t mask) {
   return kLargest ? (key & mask) >= prefix : (key & mask) <= prefix;
+}
+
+// Top-B threshold bin from a complete score histogram (kScoreBins linear bins
+// over [-1, 1]): bin b* holding the B_eff-th largest score, the number of
+// keys above it, and how many of b*'s keys are still needed. Block of NT
+// threads; every thread returns the same values.
+template <int NT>
+__device__ void find_threshold_bin(const uint32_t* __restrict__ h, int L, int B_eff,
+                                   RadixScratch<NT>& rs, int* bstar, int* above, int* need) {
+  __shared__ int sh[3];
+  if (B_eff >= L) {
+    *bstar = -1; *above = L; *need = 0;
+    return;
+  }
+  // thread i owns PER bins counting down from the top
+  constexpr int PER = kScoreBins / NT;
+  uint32_t c[PER];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    c[e] = h[kScoreBins - 1 - (threadIdx.x * PER + e)];
+    tot += c[e];
+  }
+  uint32_t cum = block_exclusive_scan<NT>(tot, rs);  // keys in higher bins
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (cum < (uint32_t)B_eff && (uint32_t)B_eff <= cum + c[e]) {
+      sh[0] = kScoreBins - 1 - (threadIdx.x * PER + e);
+      sh[1] = (int)cum;
+      sh[2] = B_eff - (int)cum;
+    }
+    cum += c[e];
+  }
+  __syncthreads();
+  *bstar = sh[0]; *above = sh[1]; *need = sh[2];
+  __syncthreads();
 }
 
 }  // namespace quoka

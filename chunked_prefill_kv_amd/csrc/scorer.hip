@@ -14,6 +14,16 @@
 
 namespace quoka {
 
+// Adds the workgroup's score histogram to the problem's.
+__device__ __forceinline__ void flush_hist(const uint32_t* lhist, uint32_t* __restrict__ hist,
+                                           int prob) {
+  uint32_t* gh = hist + (int64_t)prob * kScoreBins;
+  for (int i = threadIdx.x; i < kScoreBins; i += 256) {
+    const uint32_t c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
 // bf16 keys, MFMA v_mfma_f32_16x16x32_bf16.
 //   A = kept queries [16 x 32 d] from LDS (pre-laid-out by the query select as
 //       hi and lo bf16 terms of the fp32 g, so g ~ hi + lo to 2^-16),
@@ -131,11 +141,7 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     }
   }
   __syncthreads();
-  uint32_t* gh = hist + (int64_t)prob * kScoreBins;
-  for (int i = threadIdx.x; i < kScoreBins; i += 256) {
-    const uint32_t c = lhist[i];
-    if (c) atomicAdd(&gh[i], c);
-  }
+  flush_hist(lhist, hist, prob);
 }
 
 // fp32 keys (and any dtype as a reference path): one key per thread, kept
@@ -186,11 +192,7 @@ __global__ __launch_bounds__(256) void scorer_valu_kernel(
     atomicAdd(&lhist[score_bin(sc)], 1u);
   }
   __syncthreads();
-  uint32_t* gh = hist + (int64_t)prob * kScoreBins;
-  for (int i = threadIdx.x; i < kScoreBins; i += 256) {
-    const uint32_t c = lhist[i];
-    if (c) atomicAdd(&gh[i], c);
-  }
+  flush_hist(lhist, hist, prob);
 }
 
 hipError_t set_scorer_lds_limit(int bytes) {
