@@ -53,15 +53,54 @@ def attention_flops(w) -> float:
     return 4.0 * w.head_dim * w.num_q_heads * pairs
 
 
+def _elem(w) -> int:
+    return 2 if w.dtype == "bf16" else 4
+
+
 def scorer_bytes(w) -> float:
     """Algorithmic HBM bytes of the scorer: every history key once, plus the scores."""
-    elem = 2 if w.dtype == "bf16" else 4
-    return w.k_hist.shape[0] * w.num_kv_heads * (w.head_dim * elem + 4)
+    return w.k_hist.shape[0] * w.num_kv_heads * (w.head_dim * _elem(w) + 4)
 
 
-def cpu_baseline(w, max_heads: int = 2):
-    """The fp64 oracle on KV heads 0..max_heads-1 of sequence 0 (selection and
-    attention of their query heads); scaled to the whole layer's tokens/s."""
+def attention_bytes(w) -> float:
+    """Algorithmic HBM bytes of the chunk attention: Q, K/V_sel, K/V_chunk read once, O written once."""
+    tc = int(w.cu_chunk[-1])
+    sel_rows = w.num_seqs * w.num_kv_heads * w.budget
+    return _elem(w) * w.head_dim * (2 * tc * w.num_q_heads + 2 * sel_rows + 2 * tc * w.num_kv_heads)
+
+
+def gather_bytes(w) -> float:
+    """Algorithmic HBM bytes of the gather: the selected K and V rows read, K/V_sel written
+    (padding rows past B_eff are written only), plus the indices."""
+    sel = sum(min(w.budget, int(L)) for L in w.hist_lens) * w.num_kv_heads
+    rows = w.num_seqs * w.num_kv_heads * w.budget
+    return _elem(w) * w.head_dim * 2 * (sel + rows) + 4 * rows
+
+
+def measured_traffic(config: str, kernel: str, source: str):
+    """HBM bytes per launch from the committed counter runs (profiles/hbm_traffic.md), or
+    None when they are missing or the kernel source changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    try:
+        text = open(path).read()
+        block = text[text.index("```json") + 7:]
+        data = json.loads(block[:block.index("```")])
+        rec = data[config][kernel]
+        csrc = os.path.join(ROOT, "chunked_prefill_kv_amd", "csrc")
+        for f, want in ((source, rec["source"]["sha256_16"]),
+                        ("common.h", rec["source"]["common.h"])):
+            got = hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()[:16]
+            if got != want:
+                return None
+        return float(rec["hbm_bytes"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_runs: int = 5):
+    """The fp64 oracle over the whole layer (every KV head and its query heads: selection
+    and attention), repeated until about min_seconds of CPU work; median run time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -69,21 +108,23 @@ def cpu_baseline(w, max_heads: int = 2):
     except Exception:  # pragma: no cover
         threads = 1
     cores = len(os.sched_getaffinity(0))
-    heads = list(range(min(max_heads, w.num_kv_heads)))
-    t0 = time.perf_counter()
-    oracle.prefill_chunk(w.q, w.k_hist, w.v_hist, w.k_chunk, w.v_chunk, w.cu_chunk,
-                         w.cu_hist, w.num_kv_heads, w.n_q, w.budget, heads=heads)
-    dt = time.perf_counter() - t0
-    layer_s = dt * w.num_kv_heads / len(heads)
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_runs and (not times or time.perf_counter() - t_all < min_seconds):
+        t0 = time.perf_counter()
+        oracle.prefill_chunk(w.q, w.k_hist, w.v_hist, w.k_chunk, w.v_chunk, w.cu_chunk,
+                             w.cu_hist, w.num_kv_heads, w.n_q, w.budget)
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
     return {
-        "value": float(w.cu_chunk[-1]) / layer_s,
+        "value": float(w.cu_chunk[-1]) / med,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle, whole path for KV heads {heads} of {w.num_kv_heads} "
-                   f"({len(heads) * w.num_q_heads // w.num_kv_heads} query heads), "
-                   f"{dt:.1f} s, scaled by {w.num_kv_heads}/{len(heads)} to the layer; "
-                   f"host has {cores} cores, BLAS used {threads} threads"),
+        "sample": (f"fp64 NumPy oracle, whole path for the whole layer (all {w.num_kv_heads} KV "
+                   f"heads, {w.num_q_heads} query heads), {len(times)} runs, median {med:.2f} s, "
+                   f"total {sum(times):.1f} s; host has {cores} cores, BLAS used {threads} "
+                   f"threads, the rest of the oracle runs on one"),
     }
 
 
@@ -175,7 +216,9 @@ def main():
     flops = attention_flops(w)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     achieved = flops / (att_us * 1e-6) / 1e12
-    gather_bytes = 2.0 * 2 * S * Hkv * B * w.head_dim * (2 if w.dtype == "bf16" else 4)
+    attn_kernel = "attn_mfma_kernel" if w.dtype == "bf16" else "attn_valu_kernel"
+    traffic = measured_traffic(args.config, attn_kernel, "attention.hip")
+    gbytes = gather_bytes(w)
     line = {
         "metric": "chunk-prefill attn tokens/sec per layer (select+gather+attn); "
                   "HBM/MFMA % of peak",
@@ -197,14 +240,14 @@ def main():
                    "input_sets": len(sets)},
         "stages_us": {"select": round(sel_us, 2), "gather": round(gat_us, 2),
                       "chunk_attn": round(att_us, 2)},
-        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel" if w.dtype == "bf16"
-                     else "attn_valu_kernel",
+        "roofline": {"bound": "mfma", "kernel": attn_kernel,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
-                     "algorithmic": {"flops_per_launch": flops}},
-        "secondary": {"gather_GBps": gather_bytes / (gat_us * 1e-6) / 1e9,
-                      "gather_frac_hbm": gather_bytes / (gat_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                      "scorer_bytes": scorer_bytes(w)},
+                     "frac": achieved / peak, "traffic": traffic,
+                     "algorithmic": {"flops_per_launch": flops,
+                                     "bytes_per_launch": attention_bytes(w)}},
+        "secondary": {"gather_GBps": gbytes / (gat_us * 1e-6) / 1e9,
+                      "gather_frac_hbm": gbytes / (gat_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                      "gather_bytes": gbytes, "scorer_bytes": scorer_bytes(w)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
