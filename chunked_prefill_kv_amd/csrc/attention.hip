@@ -12,6 +12,8 @@
 #include "common.h"
 #include "internal.h"
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 namespace quoka {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -93,14 +95,15 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 
 // ---------------------------------------------------------------------------
 // MFMA path (bf16): flash-style online softmax on v_mfma_f32_32x32x16_bf16.
-// A workgroup of 4 waves owns 128 packed query rows of one (sequence, KV
-// head); row r is token r / G, query head h*G + r % G, so the G heads that
-// share the KV head share every K/V tile. Each wave owns 32 rows.
+// A workgroup of NW waves (4 or 8) owns NW*32 packed query rows of one
+// (sequence, KV head); row r is token r / G, query head h*G + r % G, so the G
+// heads that share the KV head share every K/V tile. Each wave owns 32 rows.
 //   S^T = K Q^T  : A = K tile rows from LDS, B = the wave's Q held in VGPRs,
 //                  C lane l = query column l%32, 16 key rows.
 //   O^T += V^T P^T: A = V^T via LDS transpose reads of row-major V, B = P taken straight
 //                  from the S^T accumulators; the 16 keys of a k-step are the
 //                  ones the lane already holds, so P never leaves registers.
+//                  Row sums are dot products of the bf16 P pairs.
 // K/V tiles of 64 keys: first the kept history (masked past B_eff), then the
 // chunk's keys up to the workgroup's last token (causal mask per row, only
 // on tiles that reach past a wave's first token). LDS is double buffered:
@@ -109,32 +112,33 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 // Blocks are renumbered so that all tiles of one KV head run on one XCD
 // (blocks are dealt round-robin to the 8 XCDs) and share its L2.
 // ---------------------------------------------------------------------------
-constexpr int kAttnRows = 128;
 constexpr int kXcds = 8;
 
-template <int D>
+template <int D, int NW>
 struct AttnTile {
   static constexpr int KT = 64;                  // keys per tile
+  static constexpr int NT = NW * 64;             // threads
+  static constexpr int ROWS = NW * 32;           // query rows per workgroup
   static constexpr int KSTR = D + 8;             // K row stride in LDS (elements)
   static constexpr int VSTR = D + 32;            // V row stride in LDS (elements)
-  static constexpr int NCH = KT * D / 8 / 256;   // 16-byte chunks per thread, K and V each
+  static constexpr int NCH = KT * D / 8 / NT;    // 16-byte chunks per thread, K and V each
   static constexpr int K_ELEMS = KT * KSTR;
   static constexpr int V_ELEMS = KT * VSTR;
 };
 
-// Global -> registers: thread takes 16-byte chunks c = tid + 256 i of the
+// Global -> registers: thread takes 16-byte chunks c = tid + NT i of the
 // 64 x D tile (row c / (D/8)). The buffer resources start at the tile's first
 // row and end at the last valid row, so rows past the end read as zeros
 // without any per-element select.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                                uint32_t row_bytes,
-                                               bf16x8 (&kr)[AttnTile<D>::NCH],
-                                               bf16x8 (&vr)[AttnTile<D>::NCH]) {
-  using TT = AttnTile<D>;
+                                               bf16x8 (&kr)[AttnTile<D, NW>::NCH],
+                                               bf16x8 (&vr)[AttnTile<D, NW>::NCH]) {
+  using TT = AttnTile<D, NW>;
 #pragma unroll
   for (int i = 0; i < TT::NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
+    const int c = threadIdx.x + TT::NT * i;
     const uint32_t off = (uint32_t)(c / (D / 8)) * row_bytes + (uint32_t)(c % (D / 8)) * 16u;
     kr[i] = buffer_load_bf16x8(rk, off);
     vr[i] = buffer_load_bf16x8(rv, off);
@@ -143,14 +147,14 @@ __device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t rk, __amdg
 
 // Registers -> LDS, both row-major (key, d). V is transposed later by the
 // LDS transpose read that feeds the P.V MFMA.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void attn_store_tile(bf16* __restrict__ Ks, bf16* __restrict__ Vs,
-                                                const bf16x8 (&kr)[AttnTile<D>::NCH],
-                                                const bf16x8 (&vr)[AttnTile<D>::NCH]) {
-  using TT = AttnTile<D>;
+                                                const bf16x8 (&kr)[AttnTile<D, NW>::NCH],
+                                                const bf16x8 (&vr)[AttnTile<D, NW>::NCH]) {
+  using TT = AttnTile<D, NW>;
 #pragma unroll
   for (int i = 0; i < TT::NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
+    const int c = threadIdx.x + TT::NT * i;
     const int row = c / (D / 8), part = c % (D / 8);
     *(bf16x8*)&Ks[row * TT::KSTR + part * 8] = kr[i];
     *(bf16x8*)&Vs[row * TT::VSTR + part * 8] = vr[i];
@@ -169,14 +173,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_sel, const bf16* __restrict__ v_sel,
     const bf16* __restrict__ k_chunk, const bf16* __restrict__ v_chunk,
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int S, int Hq,
     int Hkv, int G, int kv_budget, int ntile_max, float scale_log2, bf16* __restrict__ out) {
-  using TT = AttnTile<D>;
+  using TT = AttnTile<D, NW>;
   constexpr int KT = TT::KT, NDS = D / 16, NDB = D / 32;
+  constexpr int kAttnRows = TT::ROWS;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][TT::K_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][TT::V_ELEMS];
 
@@ -243,16 +248,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint32_t left = (ph1 ? end1 : end2) - skip;
     const bf16* kp = (ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2);
     const bf16* vp = (ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2);
-    attn_load_tile<D>(make_rsrc(kp, left), make_rsrc(vp, left), rb, kr, vr);
+    attn_load_tile<D, NW>(make_rsrc(kp, left), make_rsrc(vp, left), rb, kr, vr);
   };
   load(0);
-  attn_store_tile<D>(Ks[0], Vs[0], kr, vr);
+  attn_store_tile<D, NW>(Ks[0], Vs[0], kr, vr);
   __syncthreads();
 
   // lane-constant parts of the LDS read addresses
   const int g16 = lane >> 4, j16 = lane & 15;
   const int k_rd = col * TT::KSTR + hi * 8;                                  // K rows for S^T
   const int v_rd = (hi * 4 + (j16 >> 2)) * TT::VSTR + (g16 & 1) * 16 + 4 * (j16 & 3);
+  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
   for (int it = 0; it < n_all; ++it) {
     const int buf = it & 1;
@@ -324,9 +330,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sb][i * 4 + jj], scale_log2, -base));
-          l_part += p;
           pb[sb][i >> 1][(i & 1) * 4 + jj] = (bf16)p;
         }
+    // row sums of the bf16 P actually multiplied, two keys per instruction
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 v = pb[sb][kk];
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, l_part, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, l_part, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, l_part, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, l_part, false);
+      }
     __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T; the A operand is read transposed from row-major V: lane
     // group g = lane/16 covers d0 = db*32 + (g&1)*16, keys kb0 = ... + hi*4
@@ -347,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pb[sb][kk], oacc[db], 0, 0, 0);
       }
     __builtin_amdgcn_s_setprio(0);
-    if (it + 1 < n_all) attn_store_tile<D>(Ks[buf ^ 1], Vs[buf ^ 1], kr, vr);
+    if (it + 1 < n_all) attn_store_tile<D, NW>(Ks[buf ^ 1], Vs[buf ^ 1], kr, vr);
     __syncthreads();
   }
 
@@ -367,20 +383,30 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   }
 }
 
+// Eight-wave workgroups share each K/V tile between twice the rows (half the
+// LDS writes and L2 reads per row) but hold twice the rows, so a shape has
+// half as many of them; they are used when that still leaves two per CU
+// (with one per CU, the causal spread of work between tiles is exposed).
+constexpr int kAttnWideMinBlocks = 512;
+
 hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
                             const void* v_sel, const void* k_chunk, const void* v_chunk,
                             float scale, void* out, hipStream_t st) {
   if (p.maxC == 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (p.dtype == QUOKA_BF16) {
-    const int ntile = (int)(((int64_t)p.maxC * p.G + kAttnRows - 1) / kAttnRows);
+    const int64_t rows = (int64_t)p.maxC * p.G;
+    const bool wide = (rows + 255) / 256 * p.Hkv * p.S >= kAttnWideMinBlocks;
+    const int nw = wide ? 8 : 4;
+    const int ntile = (int)((rows + nw * 32 - 1) / (nw * 32));
     dim3 grid((unsigned)(ntile * p.Hkv * p.S));
-#define QUOKA_ATTN(D)                                                                       \
-  hipLaunchKernelGGL((attn_mfma_kernel<D>), grid, dim3(256), 0, st, (const bf16*)q,         \
-                     (const bf16*)k_sel, (const bf16*)v_sel, (const bf16*)k_chunk,          \
-                     (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,    \
+#define QUOKA_ATTN(D, NW)                                                                    \
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), grid, dim3(NW * 64), 0, st, (const bf16*)q,  \
+                     (const bf16*)k_sel, (const bf16*)v_sel, (const bf16*)k_chunk,           \
+                     (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,     \
                      p.kv_budget, ntile, sl2, (bf16*)out)
-    if (p.D == 128) QUOKA_ATTN(128); else QUOKA_ATTN(64);
+    if (p.D == 128) { if (wide) QUOKA_ATTN(128, 8); else QUOKA_ATTN(128, 4); }
+    else            { if (wide) QUOKA_ATTN(64, 8);  else QUOKA_ATTN(64, 4); }
 #undef QUOKA_ATTN
   } else {
     dim3 grid((unsigned)((p.maxC + 63) / 64), (unsigned)p.Hq, (unsigned)p.S);
