@@ -104,6 +104,7 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
   p->cu_hist_h = sh->cu_hist_host;
   p->NQT = p->NSB = p->NKT = 0;
   p->maxC = p->maxL = 0;
+  int64_t nsb_small = 0;
   for (int s = 0; s < S; ++s) {
     const int64_t C = (int64_t)sh->cu_chunk_host[s + 1] - sh->cu_chunk_host[s];
     const int64_t L = (int64_t)sh->cu_hist_host[s + 1] - sh->cu_hist_host[s];
@@ -111,9 +112,16 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
       return fail(QUOKA_EINVAL, "cu offsets decrease at sequence %d", s);
     p->NQT += (C + kQprepTokens - 1) / kQprepTokens;
     p->NSB += (L + kScoreKeys - 1) / kScoreKeys;
+    nsb_small += (L + kScoreKeysSmall - 1) / kScoreKeysSmall;
     p->NKT += (L + kTopbKeys - 1) / kTopbKeys;
     p->maxC = std::max<int>(p->maxC, (int)C);
     p->maxL = std::max<int>(p->maxL, (int)L);
+  }
+  // smaller scorer tiles when the large ones would leave CUs with one workgroup
+  p->score_keys = kScoreKeys;
+  if (p->NSB * p->Hkv < kScoreMinBlocks) {
+    p->score_keys = kScoreKeysSmall;
+    p->NSB = nsb_small;
   }
   p->TC = sh->cu_chunk_host[S];
   p->TL = sh->cu_hist_host[S];

@@ -12,7 +12,9 @@ namespace quoka {
 
 // Tilings (all per sequence; tiles never straddle two sequences).
 constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
-constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup
+constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup...
+constexpr int kScoreKeysSmall = 512; // ...or half as many when that fills the CUs better
+constexpr int kScoreMinBlocks = 512; // scorer workgroups wanted (two per CU)
 constexpr int kTopbKeys = 512;       // history keys per top-B workgroup
 constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
 
@@ -27,6 +29,7 @@ struct Problem {
   int64_t NQT, NSB, NKT;     // total qprep / scorer / top-B tiles over sequences
   int maxC, maxL;            // longest chunk, longest history
   int q_budget, kv_budget, nq_pad;
+  int score_keys;            // history keys per scorer workgroup (kScoreKeys or kScoreKeysSmall)
 };
 
 // Byte offsets of the workspace regions (each 256-byte aligned).

@@ -20,7 +20,7 @@ namespace quoka {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu_chunk,
                                                    const int32_t* __restrict__ cu_hist, int S,
-                                                   int32_t* __restrict__ plan,
+                                                   int score_keys, int32_t* __restrict__ plan,
                                                    uint4* __restrict__ zero, int64_t nzero16) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nzero16;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
       int C = cu_chunk[s + 1] - cu_chunk[s];
       int L = cu_hist[s + 1] - cu_hist[s];
       a += (C + kQprepTokens - 1) / kQprepTokens;
-      b += (L + kScoreKeys - 1) / kScoreKeys;
+      b += (L + score_keys - 1) / score_keys;
       c += (L + kTopbKeys - 1) / kTopbKeys;
     }
     qt[S] = a; sb[S] = b; kt[S] = c;
@@ -46,7 +46,7 @@ hipError_t launch_plan(const Problem& p, char* ws, const Workspace& w, hipStream
   int64_t n16 = (int64_t)((w.zero_end - w.zero_begin) / 16);
   int grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (n16 + 2047) / 2048));
   hipLaunchKernelGGL(plan_kernel, dim3(grid), dim3(256), 0, st, p.cu_chunk, p.cu_hist, p.S,
-                     (int32_t*)(ws + w.plan), (uint4*)(ws + w.zero_begin), n16);
+                     p.score_keys, (int32_t*)(ws + w.plan), (uint4*)(ws + w.zero_begin), n16);
   return hipGetLastError();
 }
 

@@ -31,26 +31,26 @@ __device__ __forceinline__ void flush_hist(const uint32_t* lhist, uint32_t* __re
 //       contiguous bytes of one key row; 4 lanes cover 64 B of a row),
 //   C = [16 queries x 16 keys]; lane l holds key column l%16, so the max over
 //       queries is a per-lane max followed by two cross-lane steps.
-// One workgroup = 4 waves = up to kScoreKeys keys of one (sequence, KV head).
+// One workgroup = 4 waves = up to KEYS keys of one (sequence, KV head).
 // Each wave streams 64-key blocks (4 MFMA blocks of 16 keys): the next block
 // is in flight while the current one is scored. Keys are read through a
 // buffer resource that ends at the sequence's last key, so reads past it
 // return zeros (those keys are never written).
-template <int D>
+template <int D, int KEYS>
 __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     const bf16* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int q_budget, int nq_pad, const bf16x8* __restrict__ gsel,
     float* __restrict__ scores, uint32_t* __restrict__ hist) {
   constexpr int NDS = D / 32;                 // d-steps per key
-  constexpr int NIT = kScoreKeys / 256;       // 64-key blocks per wave
+  constexpr int NIT = KEYS / 256;             // 64-key blocks per wave
   const int blk = blockIdx.x, h = blockIdx.y;
   const int32_t* sb_off = plan + (S + 1);
   const int s = upper_seq(sb_off, S, blk);
-  const int k_begin = (blk - sb_off[s]) * kScoreKeys;
+  const int k_begin = (blk - sb_off[s]) * KEYS;
   const int h_off = cu_hist[s];
   const int L = cu_hist[s + 1] - h_off;
-  const int k_end = min(L, k_begin + kScoreKeys);
+  const int k_end = min(L, k_begin + KEYS);
   const int n = min(q_budget, cu_chunk[s + 1] - cu_chunk[s]);
   const int nqb = (n + 15) / 16;
   const int lane = threadIdx.x & 63;
@@ -151,14 +151,14 @@ __global__ __launch_bounds__(256) void scorer_valu_kernel(
     const T* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int q_budget, int nq_pad, const float* __restrict__ gsel,
-    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int score_keys) {
   const int blk = blockIdx.x, h = blockIdx.y;
   const int32_t* sb_off = plan + (S + 1);
   const int s = upper_seq(sb_off, S, blk);
-  const int k_begin = (blk - sb_off[s]) * kScoreKeys;
+  const int k_begin = (blk - sb_off[s]) * score_keys;
   const int h_off = cu_hist[s];
   const int L = cu_hist[s + 1] - h_off;
-  const int k_end = min(L, k_begin + kScoreKeys);
+  const int k_end = min(L, k_begin + score_keys);
   const int n = min(q_budget, cu_chunk[s + 1] - cu_chunk[s]);
   const int prob = s * Hkv + h;
 
@@ -196,7 +196,10 @@ __global__ __launch_bounds__(256) void scorer_valu_kernel(
 }
 
 hipError_t set_scorer_lds_limit(int bytes) {
-  const void* fns[] = {(const void*)scorer_mfma_kernel<128>, (const void*)scorer_mfma_kernel<64>,
+  const void* fns[] = {(const void*)scorer_mfma_kernel<128, kScoreKeys>,
+                       (const void*)scorer_mfma_kernel<64, kScoreKeys>,
+                       (const void*)scorer_mfma_kernel<128, kScoreKeysSmall>,
+                       (const void*)scorer_mfma_kernel<64, kScoreKeysSmall>,
                        (const void*)scorer_valu_kernel<float, 128>,
                        (const void*)scorer_valu_kernel<float, 64>};
   for (const void* f : fns) {
@@ -215,25 +218,25 @@ hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const W
   if (p.dtype == QUOKA_BF16) {
     const size_t lds = kScoreBins * 4 + (size_t)p.nq_pad * p.D * 4;
     const bf16x8* gsel = (const bf16x8*)(ws + w.gsel);
-    if (p.D == 128)
-      hipLaunchKernelGGL((scorer_mfma_kernel<128>), grid, dim3(256), lds, st, (const bf16*)k_hist,
-                         p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL, p.q_budget, p.nq_pad,
-                         gsel, scores, hist);
-    else
-      hipLaunchKernelGGL((scorer_mfma_kernel<64>), grid, dim3(256), lds, st, (const bf16*)k_hist,
-                         p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL, p.q_budget, p.nq_pad,
-                         gsel, scores, hist);
+    const bool small = p.score_keys == kScoreKeysSmall;
+#define QUOKA_SCORER(D, K)                                                                    \
+  hipLaunchKernelGGL((scorer_mfma_kernel<D, K>), grid, dim3(256), lds, st, (const bf16*)k_hist, \
+                     p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL, p.q_budget, p.nq_pad,     \
+                     gsel, scores, hist)
+    if (p.D == 128) { if (small) QUOKA_SCORER(128, kScoreKeysSmall); else QUOKA_SCORER(128, kScoreKeys); }
+    else            { if (small) QUOKA_SCORER(64, kScoreKeysSmall);  else QUOKA_SCORER(64, kScoreKeys); }
+#undef QUOKA_SCORER
   } else {
     const size_t lds = kScoreBins * 4 + (size_t)p.q_budget * p.D * 4;
     const float* gsel = (const float*)(ws + w.gsel);
     if (p.D == 128)
       hipLaunchKernelGGL((scorer_valu_kernel<float, 128>), grid, dim3(256), lds, st,
                          (const float*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,
-                         p.q_budget, p.nq_pad, gsel, scores, hist);
+                         p.q_budget, p.nq_pad, gsel, scores, hist, p.score_keys);
     else
       hipLaunchKernelGGL((scorer_valu_kernel<float, 64>), grid, dim3(256), lds, st,
                          (const float*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,
-                         p.q_budget, p.nq_pad, gsel, scores, hist);
+                         p.q_budget, p.nq_pad, gsel, scores, hist, p.score_keys);
   }
   return hipGetLastError();
 }
