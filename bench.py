@@ -2,7 +2,9 @@
 
 A step is one pass of the whole path (query subselection, key scoring, top-B
 select, K/V gather, chunk attention) over one layer's chunk, all heads, with
-inputs already resident in HBM. Several rotated copies of the inputs are
+inputs already resident in HBM. By default the gather runs fused into the
+attention (quoka_select, then quoka_chunk_attn_gather); --unfused times the
+three separate calls (quoka_select, quoka_gather, quoka_chunk_attn). Several rotated copies of the inputs are
 cycled through so that consecutive steps do not hit the 256 MB last-level
 cache with the previous step's history keys.
 
@@ -63,10 +65,11 @@ def scorer_bytes(w) -> float:
 
 
 def attention_bytes(w) -> float:
-    """Algorithmic HBM bytes of the chunk attention: Q, K/V_sel, K/V_chunk read once, O written once."""
+    """Algorithmic HBM bytes of the chunk attention: Q, the B_eff kept K/V rows per (sequence,
+    KV head) and the chunk's K/V read once, O written once."""
     tc = int(w.cu_chunk[-1])
-    sel_rows = w.num_seqs * w.num_kv_heads * w.budget
-    return _elem(w) * w.head_dim * (2 * tc * w.num_q_heads + 2 * sel_rows + 2 * tc * w.num_kv_heads)
+    kept = sum(min(w.budget, int(L)) for L in w.hist_lens) * w.num_kv_heads
+    return _elem(w) * w.head_dim * (2 * tc * w.num_q_heads + 2 * kept + 2 * tc * w.num_kv_heads)
 
 
 def gather_bytes(w) -> float:
@@ -136,6 +139,8 @@ def main():
     ap.add_argument("--config", default="llama8b", choices=sorted(DESCR))
     ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="gather into K/V_sel and attend in separate calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the "
                          "reference for scaling HBM byte counters")
@@ -177,8 +182,10 @@ def main():
     S, Hkv, B = w.num_seqs, w.num_kv_heads, w.budget
     ws = cpk.alloc_workspace(shape, w.n_q, B)
     sel = torch.empty((S, Hkv, B), dtype=torch.int32, device=dev)
-    k_sel = torch.empty((S, Hkv, B, w.head_dim), dtype=dt, device=dev)
-    v_sel = torch.empty_like(k_sel)
+    k_sel = v_sel = None
+    if args.unfused:
+        k_sel = torch.empty((S, Hkv, B, w.head_dim), dtype=dt, device=dev)
+        v_sel = torch.empty_like(k_sel)
     out = torch.empty_like(base["q"])
 
     def step(i, ev=None):
@@ -188,10 +195,15 @@ def main():
         cpk.select(shape, x["q"], x["k_hist"], w.n_q, B, sel_idx=sel, workspace=ws)
         if ev is not None:
             ev[1].record()
-        cpk.gather(shape, x["k_hist"], x["v_hist"], sel, B, k_sel=k_sel, v_sel=v_sel)
+        if args.unfused:
+            cpk.gather(shape, x["k_hist"], x["v_hist"], sel, B, k_sel=k_sel, v_sel=v_sel)
         if ev is not None:
             ev[2].record()
-        cpk.chunk_attn(shape, x["q"], k_sel, v_sel, B, x["k_chunk"], x["v_chunk"], out=out)
+        if args.unfused:
+            cpk.chunk_attn(shape, x["q"], k_sel, v_sel, B, x["k_chunk"], x["v_chunk"], out=out)
+        else:
+            cpk.chunk_attn_gather(shape, x["q"], x["k_hist"], x["v_hist"], sel, B, x["k_chunk"],
+                                  x["v_chunk"], out=out)
         if ev is not None:
             ev[3].record()
 
@@ -237,17 +249,22 @@ def main():
                    "chunk_tokens": int(tokens), "history_tokens": int(TL),
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "q_budget": w.n_q, "kv_budget": B,
-                   "input_sets": len(sets)},
-        "stages_us": {"select": round(sel_us, 2), "gather": round(gat_us, 2),
-                      "chunk_attn": round(att_us, 2)},
+                   "input_sets": len(sets),
+                   "path": "select + gather + chunk_attn" if args.unfused
+                           else "select + chunk_attn_gather (gather fused)"},
+        "stages_us": ({"select": round(sel_us, 2), "gather": round(gat_us, 2),
+                       "chunk_attn": round(att_us, 2)} if args.unfused else
+                      {"select": round(sel_us, 2), "chunk_attn_gather": round(att_us, 2)}),
         "roofline": {"bound": "mfma", "kernel": attn_kernel,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "algorithmic": {"flops_per_launch": flops,
                                      "bytes_per_launch": attention_bytes(w)}},
-        "secondary": {"gather_GBps": gbytes / (gat_us * 1e-6) / 1e9,
-                      "gather_frac_hbm": gbytes / (gat_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                      "gather_bytes": gbytes, "scorer_bytes": scorer_bytes(w)},
+        "secondary": ({"gather_GBps": gbytes / (gat_us * 1e-6) / 1e9,
+                       "gather_frac_hbm": gbytes / (gat_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                       "gather_bytes": gbytes} if args.unfused else
+                      {"gather": "fused into the attention (quoka_chunk_attn_gather)"}) |
+                     {"scorer_bytes": scorer_bytes(w)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

@@ -25,7 +25,7 @@ QUOKA_F32, QUOKA_BF16 = 0, 1
 MAX_Q_BUDGET = 128
 
 SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_gather", "quoka_chunk_attn",
-           "quoka_prefill_chunk", "quoka_strerror", "quoka_last_error")
+           "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_strerror", "quoka_last_error")
 
 
 class QuokaError(RuntimeError):
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.quoka_select.argtypes = [sp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.quoka_gather.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp]
     lib.quoka_chunk_attn.argtypes = [sp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp]
+    lib.quoka_chunk_attn_gather.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
+                                            vp]
     lib.quoka_prefill_chunk.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
                                         vp, vp, sz, vp]
     for f in ("quoka_workspace_bytes", "quoka_select", "quoka_gather", "quoka_chunk_attn",
@@ -223,6 +225,27 @@ def chunk_attn(shape: Shape, q, k_sel, v_sel, kv_budget: int, k_chunk, v_chunk,
     _check(lib.quoka_chunk_attn(ctypes.byref(shape.c), _ptr(q), _ptr(k_sel), _ptr(v_sel),
                                 kv_budget, _ptr(k_chunk), _ptr(v_chunk), float(softmax_scale),
                                 _ptr(out), _stream(shape.device)), "quoka_chunk_attn")
+    return out
+
+
+def chunk_attn_gather(shape: Shape, q, k_hist, v_hist, sel_idx, kv_budget: int, k_chunk,
+                      v_chunk, softmax_scale: float = 0.0, *, out=None):
+    """Gather fused into the chunk attention: equals gather() then chunk_attn()."""
+    lib = load_library()
+    S, Hq, Hkv, d = shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    shape._check_tensor(q, "q", (shape.total_chunk, Hq, d), shape.torch_dtype)
+    for t, n in ((k_hist, "k_hist"), (v_hist, "v_hist")):
+        shape._check_tensor(t, n, (shape.total_hist, Hkv, d), shape.torch_dtype)
+    shape._check_tensor(sel_idx, "sel_idx", (S, Hkv, kv_budget), torch.int32)
+    for t, n in ((k_chunk, "k_chunk"), (v_chunk, "v_chunk")):
+        shape._check_tensor(t, n, (shape.total_chunk, Hkv, d), shape.torch_dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    shape._check_tensor(out, "out", tuple(q.shape), shape.torch_dtype)
+    _check(lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), _ptr(q), _ptr(k_hist),
+                                       _ptr(v_hist), _ptr(sel_idx), kv_budget, _ptr(k_chunk),
+                                       _ptr(v_chunk), float(softmax_scale), _ptr(out),
+                                       _stream(shape.device)), "quoka_chunk_attn_gather")
     return out
 
 

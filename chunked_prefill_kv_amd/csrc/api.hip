@@ -151,7 +151,6 @@ Workspace workspace_layout(const Problem& p) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  const size_t elem = p.dtype == QUOKA_BF16 ? 2 : 4;
   const size_t SH = (size_t)p.S * p.Hkv;
   w.plan = take(3 * (size_t)(p.S + 1) * 4);
   w.g = take((size_t)p.TC * p.Hkv * p.D * 4);
@@ -170,8 +169,6 @@ Workspace workspace_layout(const Problem& p) {
   w.gtcount = take((size_t)p.Hkv * p.NKT * 4);
   w.select_end = o;
   w.selidx = take(SH * p.kv_budget * 4);
-  w.ksel = take(SH * p.kv_budget * p.D * elem);
-  w.vsel = take(SH * p.kv_budget * p.D * elem);
   w.total = o;
   return w;
 }
@@ -270,8 +267,31 @@ quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q, const voi
   QUOKA_NEED(out, p.TC);
   if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
-  return hip_check(launch_attention(p, q, k_sel, v_sel, k_chunk, v_chunk, scale, out, stream),
-                   "attention", stream);
+  return hip_check(
+      launch_attention(p, q, k_sel, v_sel, nullptr, k_chunk, v_chunk, scale, out, stream),
+      "attention", stream);
+}
+
+quoka_status quoka_chunk_attn_gather(const quoka_shape* shape, const void* q, const void* k_hist,
+                                     const void* v_hist, const int32_t* sel_idx,
+                                     int32_t kv_budget, const void* k_chunk, const void* v_chunk,
+                                     float softmax_scale, void* out, hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, 1, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(q, p.TC);
+  QUOKA_NEED(k_hist, p.TL);
+  QUOKA_NEED(v_hist, p.TL);
+  QUOKA_NEED(sel_idx, 1);
+  QUOKA_NEED(k_chunk, p.TC);
+  QUOKA_NEED(v_chunk, p.TC);
+  QUOKA_NEED(out, p.TC);
+  if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
+  return hip_check(
+      launch_attention(p, q, k_hist, v_hist, sel_idx, k_chunk, v_chunk, scale, out, stream),
+      "attention", stream);
 }
 
 quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q, const void* k_hist,
@@ -299,13 +319,10 @@ quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q, const 
   int32_t* sel = sel_idx_opt ? sel_idx_opt : (int32_t*)(base + w.selidx);
   rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
   if (rc != QUOKA_OK) return rc;
-  void* ks = base + w.ksel;
-  void* vs = base + w.vsel;
-  rc = hip_check(launch_gather(p, k_hist, v_hist, sel, ks, vs, stream), "gather", stream);
-  if (rc != QUOKA_OK) return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
-  return hip_check(launch_attention(p, q, ks, vs, k_chunk, v_chunk, scale, out, stream),
-                   "attention", stream);
+  return hip_check(
+      launch_attention(p, q, k_hist, v_hist, sel, k_chunk, v_chunk, scale, out, stream),
+      "attention", stream);
 }
 
 const char* quoka_strerror(quoka_status status) {

@@ -26,7 +26,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k_sel, const T* __restrict__ v_sel,
-    const T* __restrict__ k_chunk, const T* __restrict__ v_chunk,
+    const int32_t* __restrict__ sel, const T* __restrict__ k_chunk, const T* __restrict__ v_chunk,
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int Hq, int Hkv,
     int G, int kv_budget, float scale_log2, T* __restrict__ out) {
   constexpr int KT = 32;
@@ -37,8 +37,8 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
   const int C = cu_chunk[s + 1] - c_off;
   const int t0 = blockIdx.x * 64;
   if (t0 >= C) return;
-  const int h_off = cu_hist[s];
-  const int L = cu_hist[s + 1] - h_off;
+  const int L_off = cu_hist[s];
+  const int L = cu_hist[s + 1] - L_off;
   const int B_eff = min(kv_budget, L);
   const int lane = threadIdx.x;
   const int t = t0 + lane;
@@ -57,16 +57,26 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 
   for (int phase = 0; phase < 2; ++phase) {
     const int nkeys = phase == 0 ? B_eff : t_end;
-    const T* kb = phase == 0 ? k_sel + prob * kv_budget * D : k_chunk + ((int64_t)c_off * Hkv + h) * D;
-    const T* vb = phase == 0 ? v_sel + prob * kv_budget * D : v_chunk + ((int64_t)c_off * Hkv + h) * D;
-    const int64_t stride = phase == 0 ? D : (int64_t)Hkv * D;
+    // history rows: kept rows of k_sel / v_sel, or (sel given) rows sel[b] of
+    // this sequence's k_hist / v_hist passed in their place
+    const bool indexed = phase == 0 && sel != nullptr;
+    const T* kb = phase == 1 ? k_chunk + ((int64_t)c_off * Hkv + h) * D
+                  : indexed ? k_sel + ((int64_t)L_off * Hkv + h) * D : k_sel + prob * kv_budget * D;
+    const T* vb = phase == 1 ? v_chunk + ((int64_t)c_off * Hkv + h) * D
+                  : indexed ? v_sel + ((int64_t)L_off * Hkv + h) * D : v_sel + prob * kv_budget * D;
+    const int64_t stride = (phase == 0 && !indexed) ? D : (int64_t)Hkv * D;
     for (int k0 = 0; k0 < nkeys; k0 += KT) {
       __syncthreads();
       for (int idx = lane; idx < KT * D; idx += 64) {
         const int r = idx / D, c = idx % D;
-        const bool ok = k0 + r < nkeys;
-        Ks[r][c] = ok ? to_f32(kb[(int64_t)(k0 + r) * stride + c]) : 0.f;
-        Vs[r][c] = ok ? to_f32(vb[(int64_t)(k0 + r) * stride + c]) : 0.f;
+        int row = k0 + r;
+        bool ok = row < nkeys;
+        if (indexed && ok) {
+          row = sel[prob * kv_budget + row];
+          ok = (unsigned)row < (unsigned)L;
+        }
+        Ks[r][c] = ok ? to_f32(kb[(int64_t)row * stride + c]) : 0.f;
+        Vs[r][c] = ok ? to_f32(vb[(int64_t)row * stride + c]) : 0.f;
       }
       __syncthreads();
       const int kn = min(KT, nkeys - k0);
@@ -173,10 +183,10 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-template <int D, int NW>
+template <int D, int NW, bool kIdx>
 __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_sel, const bf16* __restrict__ v_sel,
-    const bf16* __restrict__ k_chunk, const bf16* __restrict__ v_chunk,
+    const int32_t* __restrict__ sel, const bf16* __restrict__ k_chunk, const bf16* __restrict__ v_chunk,
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int S, int Hq,
     int Hkv, int G, int kv_budget, int ntile_max, float scale_log2, bf16* __restrict__ out) {
   using TT = AttnTile<D, NW>;
@@ -229,20 +239,52 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   float m_run = -INFINITY, l_part = 0.f;
 
   const int64_t prob = (int64_t)s * Hkv + h;
-  const bf16* k1 = k_sel + prob * kv_budget * D;
-  const bf16* v1 = v_sel + prob * kv_budget * D;
+  // history rows: the kept rows of k_sel / v_sel, or (kIdx) rows sel[b] of
+  // this sequence's k_hist / v_hist, passed in their place (gather fused in)
+  const bf16* k1 = kIdx ? k_sel + ((int64_t)h_off * Hkv + h) * D : k_sel + prob * kv_budget * D;
+  const bf16* v1 = kIdx ? v_sel + ((int64_t)h_off * Hkv + h) * D : v_sel + prob * kv_budget * D;
   const bf16* k2 = k_chunk + ((int64_t)c_off * Hkv + h) * D;
   const bf16* v2 = v_chunk + ((int64_t)c_off * Hkv + h) * D;
   const int n1 = (B_eff + KT - 1) / KT;
   const int n_all = n1 + (t_last + KT) / KT;
-  const uint32_t rb1 = D * 2u, rb2 = (uint32_t)Hkv * D * 2u;            // row bytes
-  const uint32_t end1 = (uint32_t)B_eff * rb1;                           // valid bytes
+  const uint32_t rb1 = kIdx ? (uint32_t)Hkv * D * 2u : D * 2u;           // row bytes
+  const uint32_t rb2 = (uint32_t)Hkv * D * 2u;
+  const uint32_t end1 = kIdx ? (Lh > 0 ? (uint32_t)(Lh - 1) * rb1 + D * 2u : 0u)  // valid bytes
+                             : (uint32_t)B_eff * rb1;
   const uint32_t end2 = (uint32_t)t_last * rb2 + D * 2u;
+  const int32_t* sidx = sel + prob * kv_budget;
 
   bf16x8 kr[TT::NCH], vr[TT::NCH];
+  // kIdx: history row indices of the next tile to load, fetched one tile
+  // ahead so that a row load never waits for its own index load
+  int nidx[TT::NCH];
+  auto fetch_idx = [&](int it) {
+#pragma unroll
+    for (int i = 0; i < TT::NCH; ++i) {
+      const int key = it * KT + (int)(threadIdx.x + TT::NT * i) / (D / 8);
+      nidx[i] = key < B_eff ? sidx[key] : -1;
+    }
+  };
+  if (kIdx && n1 > 0) fetch_idx(0);
   auto load = [&](int it) {
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
+    if (kIdx && ph1) {
+      // row of key kbase + r is history row sel[kbase + r]; padding (-1) and
+      // out-of-range indices read at the end of the buffer, i.e. as zeros
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k1, end1), rv = make_rsrc(v1, end1);
+#pragma unroll
+      for (int i = 0; i < TT::NCH; ++i) {
+        const int c = threadIdx.x + TT::NT * i;
+        const int row = nidx[i];
+        const uint32_t off = (unsigned)row < (unsigned)Lh
+                                 ? (uint32_t)row * rb1 + (uint32_t)(c % (D / 8)) * 16u : end1;
+        kr[i] = buffer_load_bf16x8(rk, off);
+        vr[i] = buffer_load_bf16x8(rv, off);
+      }
+      if (it + 1 < n1) fetch_idx(it + 1);
+      return;
+    }
     const uint32_t rb = ph1 ? rb1 : rb2;
     const uint32_t skip = (uint32_t)kbase * rb;
     const uint32_t left = (ph1 ? end1 : end2) - skip;
@@ -390,8 +432,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
 constexpr int kAttnWideMinBlocks = 512;
 
 hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
-                            const void* v_sel, const void* k_chunk, const void* v_chunk,
-                            float scale, void* out, hipStream_t st) {
+                            const void* v_sel, const int32_t* sel, const void* k_chunk,
+                            const void* v_chunk, float scale, void* out, hipStream_t st) {
   if (p.maxC == 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (p.dtype == QUOKA_BF16) {
@@ -400,19 +442,21 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
     const int nw = wide ? 8 : 4;
     const int ntile = (int)((rows + nw * 32 - 1) / (nw * 32));
     dim3 grid((unsigned)(ntile * p.Hkv * p.S));
-#define QUOKA_ATTN(D, NW)                                                                    \
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), grid, dim3(NW * 64), 0, st, (const bf16*)q,  \
-                     (const bf16*)k_sel, (const bf16*)v_sel, (const bf16*)k_chunk,           \
-                     (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,     \
+#define QUOKA_ATTN(D, NW, IDX)                                                                 \
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, IDX>), grid, dim3(NW * 64), 0, st, (const bf16*)q, \
+                     (const bf16*)k_sel, (const bf16*)v_sel, sel, (const bf16*)k_chunk,           \
+                     (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,          \
                      p.kv_budget, ntile, sl2, (bf16*)out)
-    if (p.D == 128) { if (wide) QUOKA_ATTN(128, 8); else QUOKA_ATTN(128, 4); }
-    else            { if (wide) QUOKA_ATTN(64, 8);  else QUOKA_ATTN(64, 4); }
+#define QUOKA_ATTN_NW(D, IDX) { if (wide) QUOKA_ATTN(D, 8, IDX); else QUOKA_ATTN(D, 4, IDX); }
+    if (sel) { if (p.D == 128) QUOKA_ATTN_NW(128, true) else QUOKA_ATTN_NW(64, true) }
+    else     { if (p.D == 128) QUOKA_ATTN_NW(128, false) else QUOKA_ATTN_NW(64, false) }
+#undef QUOKA_ATTN_NW
 #undef QUOKA_ATTN
   } else {
     dim3 grid((unsigned)((p.maxC + 63) / 64), (unsigned)p.Hq, (unsigned)p.S);
 #define QUOKA_ATTN(D)                                                                       \
   hipLaunchKernelGGL((attn_valu_kernel<float, D>), grid, dim3(64), 0, st, (const float*)q,  \
-                     (const float*)k_sel, (const float*)v_sel, (const float*)k_chunk,       \
+                     (const float*)k_sel, (const float*)v_sel, sel, (const float*)k_chunk, \
                      (const float*)v_chunk, p.cu_chunk, p.cu_hist, p.Hq, p.Hkv, p.G,        \
                      p.kv_budget, sl2, (float*)out)
     if (p.D == 128) QUOKA_ATTN(128); else QUOKA_ATTN(64);

@@ -48,8 +48,6 @@ struct Workspace {
   size_t gtcount;   // uint32 [Hkv, NKT] keys above the threshold bin per tile
   size_t chcount;   // uint32 [Hkv, NKT] chosen candidates per tile
   size_t selidx;    // int32 [S, Hkv, B]  (prefill path)
-  size_t ksel;      // elem [S, Hkv, B, D] (prefill path)
-  size_t vsel;      // elem [S, Hkv, B, D] (prefill path)
   size_t select_end, total;
   size_t zero_begin, zero_end;  // [hist .. chcount] region cleared per call
 };
@@ -81,8 +79,11 @@ hipError_t launch_topb(const Problem& p, char* ws, const Workspace& w, const flo
                        int32_t* sel_idx, hipStream_t st);
 hipError_t launch_gather(const Problem& p, const void* k_hist, const void* v_hist,
                          const int32_t* sel_idx, void* k_sel, void* v_sel, hipStream_t st);
+// sel == nullptr: history rows are k_sel / v_sel [S, Hkv, kv_budget, D];
+// otherwise k_sel / v_sel are k_hist / v_hist and row b of (s, h) is history
+// row sel[s, h, b] (gather fused into the attention).
 hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
-                            const void* v_sel, const void* k_chunk, const void* v_chunk,
-                            float scale, void* out, hipStream_t st);
+                            const void* v_sel, const int32_t* sel, const void* k_chunk,
+                            const void* v_chunk, float scale, void* out, hipStream_t st);
 
 }  // namespace quoka

@@ -139,8 +139,23 @@ quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q,
                               const void* v_chunk, float softmax_scale,
                               void* out, hipStream_t stream);
 
-/* The whole hot path (select, gather into the workspace, attend) in one call.
- * sel_idx_opt, when not null, receives the kept indices as in quoka_select. */
+/* Gather and chunk attention in one pass (the gather fused into the
+ * attention: the same result as quoka_gather followed by quoka_chunk_attn,
+ * without the k_sel / v_sel round trip through HBM). The kept history rows of
+ * (s, h) are rows sel_idx[s, h, 0 .. B_eff) of sequence s, head h of k_hist /
+ * v_hist; an index of -1 (or outside [0, L_s)) contributes a zero key and a
+ * zero value, exactly as quoka_gather's zero rows would.
+ *   softmax_scale <= 0 selects 1 / sqrt(d). */
+quoka_status quoka_chunk_attn_gather(const quoka_shape* shape, const void* q,
+                                     const void* k_hist, const void* v_hist,
+                                     const int32_t* sel_idx, int32_t kv_budget,
+                                     const void* k_chunk, const void* v_chunk,
+                                     float softmax_scale, void* out,
+                                     hipStream_t stream);
+
+/* The whole hot path (select, then attention with the gather fused in) in
+ * one call. sel_idx_opt, when not null, receives the kept indices as in
+ * quoka_select. */
 quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q,
                                  const void* k_hist, const void* v_hist,
                                  const void* k_chunk, const void* v_chunk,

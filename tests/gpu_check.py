@@ -49,9 +49,12 @@ def run_stages(w, shape, t):
                      want_scores=True)
     k_sel, v_sel = cpk.gather(shape, t["k_hist"], t["v_hist"], sel["sel_idx"], B)
     out = cpk.chunk_attn(shape, t["q"], k_sel, v_sel, B, t["k_chunk"], t["v_chunk"])
+    out_fused = cpk.chunk_attn_gather(shape, t["q"], t["k_hist"], t["v_hist"], sel["sel_idx"], B,
+                                      t["k_chunk"], t["v_chunk"])
     torch.cuda.synchronize()
     return {k: (v.cpu().float().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy())
-            for k, v in dict(sel, k_sel=k_sel, v_sel=v_sel, out=out).items() if v is not None}
+            for k, v in dict(sel, k_sel=k_sel, v_sel=v_sel, out=out, out_fused=out_fused).items()
+            if v is not None}
 
 
 def _band_check(got, want, values, boundary, band, what):

@@ -114,6 +114,10 @@ def test_null_and_misaligned_inputs_are_rejected(lib):
     assert st == cpk.QUOKA_EINVAL
     st = lib.quoka_gather(ctypes.byref(shape.c), p, p, None, 8, p, p, None)
     assert st == cpk.QUOKA_EINVAL
+    st = lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), p, p, p, None, 8, p, p, 0.0, p, None)
+    assert st == cpk.QUOKA_EINVAL and "sel_idx is null" in lib.quoka_last_error().decode()
+    st = lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), p, p, p + 4, p, 8, p, p, 0.0, p, None)
+    assert st == cpk.QUOKA_EINVAL and "aligned" in lib.quoka_last_error().decode()
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):

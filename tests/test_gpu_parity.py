@@ -49,6 +49,8 @@ def test_stage_parity(name):
     ties = check_selection(w, r)
     check_gather(w, r)
     err = check_attention(w, r)
+    # the gather fused into the attention reads the same rows in the same order
+    assert np.array_equal(r["out_fused"], r["out"]), "fused gather differs from gather + attend"
     print(f"[gpu] {name}: ties {ties}, attention max-abs {err:.3g}", flush=True)
     if w.needles.shape[0]:
         hit, total, in_s = check_needles(w, r)
@@ -66,6 +68,27 @@ def test_fused_equals_stagewise():
     torch.cuda.synchronize()
     assert np.array_equal(sel.cpu().numpy(), r["sel_idx"])
     assert np.array_equal(out.float().cpu().numpy(), r["out"])
+
+
+def test_fused_gather_handles_padding_and_bad_indices():
+    """chunk_attn_gather == gather + chunk_attn when sel_idx holds -1 padding in the middle and
+    indices outside [0, L_s) (both read as zero rows), for both kernels (bf16 MFMA, fp32)."""
+    for name in ("bf16_d128_g4_ragged", "fp32_d128_g2_ragged"):
+        print(f"[gpu] fused gather, bad indices {name}", flush=True)
+        w = _case(name)
+        shape, t = upload(w)
+        B = w.budget
+        sel = cpk.select(shape, t["q"], t["k_hist"], w.n_q, B)["sel_idx"]
+        g = torch.Generator().manual_seed(7)
+        mask = torch.rand(sel.shape, generator=g) < 0.2
+        junk = torch.randint(-5, 10**6, sel.shape, generator=g, dtype=torch.int32)
+        sel = torch.where(mask.to(sel.device), junk.to(sel.device), sel).contiguous()
+        k_sel, v_sel = cpk.gather(shape, t["k_hist"], t["v_hist"], sel, B)
+        out = cpk.chunk_attn(shape, t["q"], k_sel, v_sel, B, t["k_chunk"], t["v_chunk"])
+        fused = cpk.chunk_attn_gather(shape, t["q"], t["k_hist"], t["v_hist"], sel, B,
+                                      t["k_chunk"], t["v_chunk"])
+        torch.cuda.synchronize()
+        assert torch.equal(out, fused)
 
 
 def test_repeat_runs_are_bitwise_identical():
