@@ -43,6 +43,7 @@ DESCR = {
     "narrow": "narrow-GQA layer: 1 seq, 28q/4kv heads, d=128, bf16, L=65536, C=1024, Nq=32, "
               "B=1024",
     "ragged": "8 ragged seqs, L=4K..96K, C=512 each, 32q/8kv heads, d=128, bf16, Nq=32, B=1024",
+    "decode": "decode step: 8 seqs, C=1 each, L=16384, 32q/8kv heads, d=128, bf16, Nq=1, B=2048",
 }
 
 

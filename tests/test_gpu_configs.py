@@ -25,10 +25,11 @@ SAMPLES = {
     "narrow": ([0, 3], None, 48),
     "ragged": ([2], None, 16),
     "long": ([5], None, 32),
+    "decode": ([1, 6], None, 8),
 }
 
 
-@pytest.mark.parametrize("name", ["llama8b", "narrow", "ragged", "long"])
+@pytest.mark.parametrize("name", ["llama8b", "narrow", "ragged", "long", "decode"])
 def test_config_parity(name):
     print(f"[gpu] config {name}: generating", flush=True)
     w = make_config(name)

@@ -92,6 +92,7 @@ CONFIGS = {
     "long": 2,      # 32/8 heads, d=128, bf16, L=131072, C=4096, Nq=128, B=4096
     "narrow": 3,    # 28/4 heads, d=128, bf16, L=65536, C=1024, Nq=32, B=1024
     "ragged": 4,    # 8 seqs, L={4..96}K, C=512 each, 32/8, Nq=32, B=1024
+    "decode": 5,    # decode step (C=1): 8 seqs, 32/8 heads, d=128, bf16, L=16384, Nq=1, B=2048
 }
 
 SEED_BASE = 20260000
@@ -205,7 +206,7 @@ def make_case(seqs: Sequence[Tuple[int, int]], num_q_heads: int,
 
 
 def make_config(name: str) -> Workload:
-    """One of the five layer shapes, seeded with 20260000 + its index."""
+    """One of the layer shapes, seeded with 20260000 + its index."""
     seed = SEED_BASE + CONFIGS[name]
     if name == "tiny":
         return _make_tiny(seed)
@@ -222,6 +223,11 @@ def make_config(name: str) -> Workload:
         hist = [k * 1024 for k in (4, 8, 16, 24, 32, 48, 64, 96)]
         return make_case([(512, l) for l in hist], 32, 8, 128, "bf16", 32, 1024,
                          seed, needles_per_head=16, name=name)
+    if name == "decode":
+        # the degenerate chunk of one token: its one (kept) query scores the
+        # history; channel-scaled like llama8b
+        return make_case([(1, 16384)] * 8, 32, 8, 128, "bf16", 1, 2048, seed,
+                         scaled=True, name=name)
     raise KeyError(name)
 
 
