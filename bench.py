@@ -132,6 +132,75 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_runs: int = 5):
     }
 
 
+def bench_prompt(args):
+    """Whole-prompt chunked prefill of one sequence (llama8b heads: 32/8, d=128, bf16,
+    N_q=64, B=2048): quoka_prefill_prompt against dense chunked prefill, where every chunk
+    attends to its whole history (the same attention kernel with every history key kept)."""
+    import torch
+    import chunked_prefill_kv_amd as cpk
+    T, Bc, Hq, Hkv, d, nq, B = args.prompt, args.chunk, 32, 8, 128, 64, 2048
+    g = torch.Generator(device="cuda").manual_seed(20260100)
+    q = torch.randn(T, Hq, d, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(T, Hkv, d, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(T, Hkv, d, device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    nch = -(-T // Bc)
+    ws = None
+
+    def quoka():
+        nonlocal ws
+        if ws is None:
+            import ctypes
+            pr = cpk._CPrompt(Hq, Hkv, d, cpk.QUOKA_BF16, T, Bc)
+            sz = ctypes.c_size_t(0)
+            cpk.load_library().quoka_prompt_workspace_bytes(ctypes.byref(pr), nq, B,
+                                                            ctypes.byref(sz))
+            ws = torch.empty(sz.value, dtype=torch.uint8, device="cuda")
+        cpk.prefill_prompt(q, k, v, Bc, nq, B, out=out, workspace=ws)
+
+    dense_calls = []
+    for i in range(nch):
+        a, b = i * Bc, min(T, (i + 1) * Bc)
+        shape = cpk.Shape([0, b - a], [0, a], Hq, Hkv, d, "bf16")
+        kb = max(a, 1)
+        idx = torch.arange(kb, dtype=torch.int32, device="cuda")
+        if a == 0:
+            idx.fill_(-1)
+        idx = idx.view(1, 1, kb).expand(1, Hkv, kb).contiguous()
+        dense_calls.append((shape, a, b, kb, idx))
+
+    def dense():
+        for shape, a, b, kb, idx in dense_calls:
+            cpk.chunk_attn_gather(shape, q[a:b], k[:a], v[:a], idx, kb, k[a:b], v[a:b],
+                                  out=out[a:b])
+
+    res = {}
+    for name, fn in (("quoka", quoka), ("dense", dense)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / args.steps
+    line = {
+        "metric": "whole-prompt chunked prefill tokens/s (one layer, QUOKA selection per chunk)",
+        "value": T / (res["quoka"] * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["quoka"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v)",
+        "config": {"workload": f"prompt of {T} tokens in chunks of {Bc}, 32q/8kv heads, d=128, "
+                               f"bf16, Nq={nq}, B={B}", "chunks": nch},
+        "dense": {"ms_per_prompt": res["dense"], "tokens_per_s": T / (res["dense"] * 1e-3),
+                  "what": "every chunk attends to its whole history (no selection)"},
+        "speedup_vs_dense": res["dense"] / res["quoka"],
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +211,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="gather into K/V_sel and attend in separate calls")
+    ap.add_argument("--prompt", type=int, default=0, metavar="T",
+                    help="time a whole prompt of T tokens through chunked prefill "
+                         "(quoka_prefill_prompt) against dense chunked prefill instead")
+    ap.add_argument("--chunk", type=int, default=2048, help="chunk length for --prompt")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the "
                          "reference for scaling HBM byte counters")
@@ -163,6 +236,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
+
+    if args.prompt:
+        bench_prompt(args)
         return
 
     w = make_config(args.config)

@@ -25,13 +25,25 @@ QUOKA_F32, QUOKA_BF16 = 0, 1
 MAX_Q_BUDGET = 128
 
 SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_gather", "quoka_chunk_attn",
-           "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_strerror", "quoka_last_error")
+           "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prompt_workspace_bytes",
+           "quoka_prefill_prompt", "quoka_strerror", "quoka_last_error")
 
 
 class QuokaError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         self.status = status
         super().__init__(f"{where}: status {status} ({detail})")
+
+
+class _CPrompt(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("prompt_len", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int32),
+    ]
 
 
 class _CShape(ctypes.Structure):
@@ -72,8 +84,13 @@ def load_library(path: str = LIB_PATH):
                                             vp]
     lib.quoka_prefill_chunk.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
                                         vp, vp, sz, vp]
+    pp = ctypes.POINTER(_CPrompt)
+    lib.quoka_prompt_workspace_bytes.argtypes = [pp, i32, i32, P(sz)]
+    lib.quoka_prefill_prompt.argtypes = [pp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp,
+                                         sz, vp]
     for f in ("quoka_workspace_bytes", "quoka_select", "quoka_gather", "quoka_chunk_attn",
-              "quoka_prefill_chunk"):
+              "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prompt_workspace_bytes",
+              "quoka_prefill_prompt"):
         getattr(lib, f).restype = ctypes.c_int
     lib.quoka_strerror.argtypes = [ctypes.c_int]
     lib.quoka_strerror.restype = ctypes.c_char_p
@@ -271,4 +288,45 @@ def prefill_chunk(shape: Shape, q, k_hist, v_hist, k_chunk, v_chunk, q_budget: i
                                    float(softmax_scale), _ptr(out), _ptr(sel_idx),
                                    _ptr(workspace), workspace.numel(), _stream(shape.device)),
            "quoka_prefill_chunk")
+    return out
+
+
+def prefill_prompt(q, k, v, chunk_len: int, q_budget: int, kv_budget: int,
+                   softmax_scale: float = 0.0, *, out=None, sel_idx=None, workspace=None):
+    """Chunked prefill of one sequence's whole prompt (quoka_prefill_prompt).
+
+    q [T, H_q, d]; k, v [T, H_kv, d] on one GPU, bf16 or fp32. sel_idx, if given, receives
+    [ceil(T / chunk_len), H_kv, kv_budget] int32 (each chunk's kept history positions)."""
+    lib = load_library()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [T, heads, d]")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q has dtype {q.dtype}; bf16 or fp32 expected")
+    for t, n, h in ((k, "k", Hkv), (v, "v", Hkv)):
+        if tuple(t.shape) != (T, h, d) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{n} must be [{T}, {h}, {d}] {q.dtype} on {q.device}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous CUDA tensor")
+    pr = _CPrompt(Hq, Hkv, d, QUOKA_BF16 if q.dtype == torch.bfloat16 else QUOKA_F32, T,
+                  chunk_len)
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    nch = -(-T // chunk_len)
+    if sel_idx is not None and (tuple(sel_idx.shape) != (nch, Hkv, kv_budget)
+                                or sel_idx.dtype != torch.int32 or not sel_idx.is_contiguous()):
+        raise ValueError(f"sel_idx must be a contiguous int32 [{nch}, {Hkv}, {kv_budget}]")
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check(lib.quoka_prompt_workspace_bytes(ctypes.byref(pr), q_budget, kv_budget,
+                                                ctypes.byref(n)), "quoka_prompt_workspace_bytes")
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
+    _check(lib.quoka_prefill_prompt(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), q_budget,
+                                    kv_budget, float(softmax_scale), _ptr(out), _ptr(sel_idx),
+                                    _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "quoka_prefill_prompt")
     return out

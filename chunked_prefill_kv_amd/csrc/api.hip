@@ -325,6 +325,114 @@ quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q, const 
       "attention", stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The workspace of a prompt: per-chunk offsets, one chunk's kept indices,
+// then the per-chunk workspace of the largest chunk problem (reused by every
+// chunk in stream order).
+struct PromptLayout {
+  int nch;
+  size_t cu, sel, chunk_ws, chunk_ws_bytes, total;
+};
+
+quoka_status prompt_layout(const quoka_prompt* pr, int32_t q_budget, int32_t kv_budget,
+                           PromptLayout* lay) {
+  if (!pr) return fail(QUOKA_EINVAL, "prompt is null");
+  if (pr->prompt_len < 1) return fail(QUOKA_EINVAL, "prompt_len=%d must be >= 1", pr->prompt_len);
+  if (pr->chunk_len < 1) return fail(QUOKA_EINVAL, "chunk_len=%d must be >= 1", pr->chunk_len);
+  const int T = pr->prompt_len, Bc = pr->chunk_len;
+  lay->nch = (int)(((int64_t)T + Bc - 1) / Bc);
+  size_t need = 0;
+  for (int i = 0; i < lay->nch; ++i) {
+    const int32_t a = (int32_t)std::min<int64_t>((int64_t)i * Bc, T);
+    const int32_t b = (int32_t)std::min<int64_t>((int64_t)a + Bc, T);
+    const int32_t cc[2] = {0, b - a}, ch[2] = {0, a};
+    // sizing only: the device offsets are not read (the host arrays stand in)
+    const quoka_shape sh = {1, pr->num_q_heads, pr->num_kv_heads, pr->head_dim, pr->dtype,
+                            cc, ch, cc, ch};
+    Problem p;
+    const quoka_status rc = make_problem(&sh, q_budget, kv_budget, &p);
+    if (rc != QUOKA_OK) return rc;
+    need = std::max(need, workspace_layout(p).total);
+  }
+  size_t o = 0;
+  lay->cu = o;
+  o = align_up(o + (size_t)lay->nch * 4 * sizeof(int32_t), 256);
+  lay->sel = o;
+  o = align_up(o + (size_t)pr->num_kv_heads * kv_budget * sizeof(int32_t), 256);
+  lay->chunk_ws = o;
+  lay->chunk_ws_bytes = need;
+  lay->total = o + need;
+  return QUOKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+quoka_status quoka_prompt_workspace_bytes(const quoka_prompt* prompt, int32_t q_budget,
+                                          int32_t kv_budget, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(QUOKA_EINVAL, "bytes is null");
+  PromptLayout lay;
+  const quoka_status rc = prompt_layout(prompt, q_budget, kv_budget, &lay);
+  if (rc != QUOKA_OK) return rc;
+  *bytes = lay.total;
+  return QUOKA_OK;
+}
+
+quoka_status quoka_prefill_prompt(const quoka_prompt* prompt, const void* q, const void* k,
+                                  const void* v, int32_t q_budget, int32_t kv_budget,
+                                  float softmax_scale, void* out, int32_t* sel_idx_opt,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  PromptLayout lay;
+  quoka_status rc = prompt_layout(prompt, q_budget, kv_budget, &lay);
+  if (rc != QUOKA_OK) return rc;
+  const int T = prompt->prompt_len, Bc = prompt->chunk_len;
+  QUOKA_NEED(q, T);
+  QUOKA_NEED(k, T);
+  QUOKA_NEED(v, T);
+  QUOKA_NEED(out, T);
+  QUOKA_NEED(sel_idx_opt, 0);
+  if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
+  if (!ws) return fail(QUOKA_EWORKSPACE, "workspace is null");
+  if (!aligned16(ws)) return fail(QUOKA_EINVAL, "workspace is not 16-byte aligned");
+  if (ws_bytes < lay.total)
+    return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, lay.total);
+  char* base = (char*)ws;
+  int32_t* cu = (int32_t*)(base + lay.cu);
+  if ((rc = hip_check(launch_prompt_offsets(T, Bc, lay.nch, cu, stream), "prompt offsets",
+                      stream)))
+    return rc;
+  const size_t elem = prompt->dtype == QUOKA_BF16 ? 2 : 4;
+  const size_t qrow = (size_t)prompt->num_q_heads * prompt->head_dim * elem;
+  const size_t krow = (size_t)prompt->num_kv_heads * prompt->head_dim * elem;
+  const size_t sel_chunk = (size_t)prompt->num_kv_heads * kv_budget;
+  for (int i = 0; i < lay.nch; ++i) {
+    const int32_t a = i * Bc, b = (int32_t)std::min<int64_t>((int64_t)a + Bc, T);
+    const int32_t cc[2] = {0, b - a}, ch[2] = {0, a};
+    const quoka_shape sh = {1, prompt->num_q_heads, prompt->num_kv_heads, prompt->head_dim,
+                            prompt->dtype, cu + 4 * i, cu + 4 * i + 2, cc, ch};
+    Problem p;
+    if ((rc = make_problem(&sh, q_budget, kv_budget, &p))) return rc;
+    const Workspace w = workspace_layout(p);
+    int32_t* sel = sel_idx_opt ? sel_idx_opt + (size_t)i * sel_chunk : (int32_t*)(base + lay.sel);
+    const char* qi = (const char*)q + (size_t)a * qrow;
+    rc = run_select(p, w, qi, k, sel, nullptr, nullptr, nullptr, base + lay.chunk_ws, stream);
+    if (rc != QUOKA_OK) return rc;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
+    if ((rc = hip_check(launch_attention(p, qi, k, v, sel, (const char*)k + (size_t)a * krow,
+                                         (const char*)v + (size_t)a * krow, scale,
+                                         (char*)out + (size_t)a * qrow, stream),
+                        "attention", stream)))
+      return rc;
+  }
+  return QUOKA_OK;
+}
+
 const char* quoka_strerror(quoka_status status) {
   switch (status) {
     case QUOKA_OK: return "success";

@@ -86,4 +86,7 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
                             const void* v_sel, const int32_t* sel, const void* k_chunk,
                             const void* v_chunk, float scale, void* out, hipStream_t st);
 
+// Per-chunk offsets {0, C_i, 0, L_i} of a one-sequence prompt split in chunks.
+hipError_t launch_prompt_offsets(int T, int chunk_len, int nch, int32_t* cu, hipStream_t st);
+
 }  // namespace quoka

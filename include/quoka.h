@@ -164,6 +164,41 @@ quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q,
                                  int32_t* sel_idx_opt, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* A whole prompt of one sequence, processed by chunked prefill. */
+typedef struct quoka_prompt {
+  int32_t num_q_heads;            /* H_q */
+  int32_t num_kv_heads;           /* H_kv */
+  int32_t head_dim;               /* d: 64 or 128 */
+  quoka_dtype dtype;
+  int32_t prompt_len;             /* T >= 1 */
+  int32_t chunk_len;              /* B_cp >= 1; the last chunk may be shorter */
+} quoka_prompt;
+
+/* Bytes of device workspace quoka_prefill_prompt needs (written to *bytes). */
+quoka_status quoka_prompt_workspace_bytes(const quoka_prompt* prompt, int32_t q_budget,
+                                          int32_t kv_budget, size_t* bytes);
+
+/* Chunked prefill of a whole prompt with QUOKA (the paper summary's
+ * "Background > Chunked prefill" and the chunked-prefill algorithm at the end
+ * of "QUOKA Method"; "QUOKA Explained", "Chunked prefill"): the prompt is cut
+ * into ceil(T / B_cp) chunks of B_cp tokens; chunk i runs the per-chunk path
+ * (quoka_prefill_chunk) with tokens [0, i B_cp) as its history, so it keeps
+ * at most kv_budget of them, and its own tokens under the causal mask. Chunk 0
+ * has no history. Nothing is evicted: every chunk selects afresh from the
+ * whole history.
+ *   q        [T, H_q, d];  k, v [T, H_kv, d]: the keys and values the prompt
+ *            writes into the cache (chunk i reads rows [0, (i+1) B_cp))
+ *   out      [T, H_q, d]
+ *   sel_idx_opt optional [ceil(T / B_cp), H_kv, kv_budget] int32: chunk i's
+ *            kept history positions, as quoka_select writes them
+ *   ws       device workspace of at least quoka_prompt_workspace_bytes(); its
+ *            contents on entry do not matter
+ * The chunks run in order on `stream`, one per-chunk pass each. */
+quoka_status quoka_prefill_prompt(const quoka_prompt* prompt, const void* q, const void* k,
+                                  const void* v, int32_t q_budget, int32_t kv_budget,
+                                  float softmax_scale, void* out, int32_t* sel_idx_opt,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* quoka_strerror(quoka_status status);
 

@@ -52,6 +52,7 @@ __all__ = [
     "unit", "cosine_matrix", "group_query", "query_cosines",
     "lowest_cosine_queries", "key_scores", "top_b_keys", "attend_rows",
     "attend_chunk", "select_for_head", "prefill_chunk", "effective_budgets",
+    "prefill_prompt",
 ]
 
 
@@ -317,3 +318,36 @@ def prefill_chunk(q, k_hist, v_hist, k_chunk, v_chunk, cu_chunk, cu_hist,
                     v_chunk[c0:c1, h, :], scale)
     return {"out": out, "q_idx": q_idx, "sel_idx": sel_idx,
             "qcos": qcos, "scores": scores}
+
+
+def prefill_prompt(q, k, v, chunk_len: int, num_kv_heads: int, n_q: int, budget: int,
+                   scale: float | None = None, **score_kw):
+    """A whole prompt of one sequence through chunked prefill with QUOKA.
+
+    [SUM] "Background > Chunked prefill": the prompt of T tokens is split into
+    ceil(T / B_cp) consecutive chunks of B_cp tokens (the last may be
+    shorter); chunk i attends to the keys and values of every earlier chunk
+    concatenated with its own, under a causal mask inside the chunk.
+    [SUM] "QUOKA Method" (the chunked-prefill algorithm at its end) and [EXP]
+    "Chunked prefill": for each new chunk QUOKA selects the active history
+    KVs from all earlier tokens (chunk 0 has no history) and passes them with
+    the chunk's own KVs to the attention; nothing is evicted, the next chunk
+    selects again from the whole history.
+
+    q [T, H_q, d]; k, v [T, H_kv, d] (the keys and values the prompt writes,
+    chunk by chunk, into the cache). Returns dict with
+      out     [T, H_q, d] float64
+      sel_idx [n_chunks, H_kv, budget] int64 (per chunk, indices into k[:start])
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T = q.shape[0]
+    n_chunks = -(-T // chunk_len)
+    out = np.empty(q.shape)
+    sel = np.full((n_chunks, int(num_kv_heads), budget), -1, np.int64)
+    for i in range(n_chunks):
+        a, b = i * chunk_len, min(T, (i + 1) * chunk_len)
+        r = prefill_chunk(q[a:b], k[:a], v[:a], k[a:b], v[a:b], [0, b - a], [0, a],
+                          num_kv_heads, n_q, budget, scale, **score_kw)
+        out[a:b] = r["out"]
+        sel[i] = r["sel_idx"][0]
+    return {"out": out, "sel_idx": sel}

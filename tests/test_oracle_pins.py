@@ -273,6 +273,53 @@ def pin_chunking_example():
     assert [c[0] for c in chunks] == ex["history_before_chunk"]
 
 
+def _dense_causal(q, k, v):
+    """Dense causal attention over a whole prompt by torch's scaled dot-product attention
+    (an independent library routine), GQA by repeating each KV head over its query heads."""
+    T, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(np.repeat(k, G, axis=1)).permute(1, 0, 2)
+    vt = torch.from_numpy(np.repeat(v, G, axis=1)).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    return o.permute(1, 0, 2).numpy()
+
+
+def pin_prompt_with_full_budget_is_dense_causal_attention():
+    """Keeping every history key, chunked prefill reproduces dense causal attention over the
+    whole prompt (the chunk masks and the history concatenation together are the causal mask)."""
+    rng = np.random.default_rng(11)
+    T, Hq, Hkv, d = 257, 4, 2, 16
+    q = rng.standard_normal((T, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    for chunk in (64, 100, 257):
+        r = oracle.prefill_prompt(q, k, v, chunk, Hkv, 8, T)
+        np.testing.assert_allclose(r["out"], _dense_causal(q, k, v), atol=1e-12)
+        n = -(-T // chunk)
+        assert r["sel_idx"].shape == (n, Hkv, T)
+        for i in range(n):  # chunk i keeps exactly its i*chunk history keys, ascending
+            kept = r["sel_idx"][i, 0]
+            assert kept[: i * chunk].tolist() == list(range(i * chunk))
+            assert np.all(kept[i * chunk:] == -1)
+
+
+def pin_prompt_chunk_zero_and_single_chunk_ignore_the_budget():
+    """Chunk 0 has no history, so a prompt that fits one chunk is dense causal attention
+    whatever the budgets; with several chunks and a small budget, chunk 0 still is."""
+    rng = np.random.default_rng(12)
+    T, Hq, Hkv, d = 80, 2, 1, 8
+    q = rng.standard_normal((T, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    dense = _dense_causal(q, k, v)
+    np.testing.assert_allclose(oracle.prefill_prompt(q, k, v, T, Hkv, 1, 1)["out"], dense,
+                               atol=1e-12)
+    r = oracle.prefill_prompt(q, k, v, 32, Hkv, 2, 3)
+    np.testing.assert_allclose(r["out"][:32], dense[:32], atol=1e-12)
+    assert not np.allclose(r["out"][64:], dense[64:])  # later chunks see only 3 history keys
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
