@@ -68,9 +68,8 @@ Workspace workspace_layout(const Problem& p);
 // queries and a score histogram on chip).
 hipError_t set_scorer_lds_limit(int bytes);
 
-hipError_t launch_plan(const Problem& p, char* ws, const Workspace& w, hipStream_t st);
-// Query prep, cosines and the lowest-cosine select; also writes the -1
-// padding of sel_idx past each problem's B_eff.
+// Plan and counter clearing, query prep, cosines and the lowest-cosine
+// select; also writes the -1 padding of sel_idx past each problem's B_eff.
 hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
                         float* qcos, int32_t* qidx, int32_t* sel_idx, hipStream_t st);
 hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const Workspace& w,

@@ -15,9 +15,30 @@ namespace quoka {
 
 // ---------------------------------------------------------------------------
 // Plan: per-sequence tile prefix sums for the three tilings, and clearing of
-// the counters the later kernels accumulate into. Block 0 plans; every block
-// clears a slice of [zero_begin, zero_end).
+// the counters the later kernels accumulate into. Query prep does both (its
+// block (0, 0) plans, all its blocks clear a slice of [zero_begin, zero_end));
+// the plan kernel covers calls where no chunk has a token.
 // ---------------------------------------------------------------------------
+// Tile prefix sums of the three tilings, by one thread.
+__device__ void write_plan(const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist,
+                           int S, int score_keys, int32_t* __restrict__ plan) {
+  int32_t* qt = plan;
+  int32_t* sb = plan + (S + 1);
+  int32_t* kt = plan + 2 * (S + 1);
+  int32_t a = 0, b = 0, c = 0;
+  for (int s = 0; s < S; ++s) {
+    qt[s] = a; sb[s] = b; kt[s] = c;
+    const int C = cu_chunk[s + 1] - cu_chunk[s];
+    const int L = cu_hist[s + 1] - cu_hist[s];
+    a += (C + kQprepTokens - 1) / kQprepTokens;
+    b += (L + score_keys - 1) / score_keys;
+    c += (L + kTopbKeys - 1) / kTopbKeys;
+  }
+  qt[S] = a; sb[S] = b; kt[S] = c;
+}
+
+// Used only when no chunk has a token (so query prep, which otherwise plans
+// and clears, has no workgroup).
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu_chunk,
                                                    const int32_t* __restrict__ cu_hist, int S,
                                                    int score_keys, int32_t* __restrict__ plan,
@@ -25,30 +46,9 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nzero16;
        i += (int64_t)gridDim.x * blockDim.x)
     zero[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    int32_t* qt = plan;
-    int32_t* sb = plan + (S + 1);
-    int32_t* kt = plan + 2 * (S + 1);
-    int32_t a = 0, b = 0, c = 0;
-    for (int s = 0; s < S; ++s) {
-      qt[s] = a; sb[s] = b; kt[s] = c;
-      int C = cu_chunk[s + 1] - cu_chunk[s];
-      int L = cu_hist[s + 1] - cu_hist[s];
-      a += (C + kQprepTokens - 1) / kQprepTokens;
-      b += (L + score_keys - 1) / score_keys;
-      c += (L + kTopbKeys - 1) / kTopbKeys;
-    }
-    qt[S] = a; sb[S] = b; kt[S] = c;
-  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) write_plan(cu_chunk, cu_hist, S, score_keys, plan);
 }
 
-hipError_t launch_plan(const Problem& p, char* ws, const Workspace& w, hipStream_t st) {
-  int64_t n16 = (int64_t)((w.zero_end - w.zero_begin) / 16);
-  int grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (n16 + 2047) / 2048));
-  hipLaunchKernelGGL(plan_kernel, dim3(grid), dim3(256), 0, st, p.cu_chunk, p.cu_hist, p.S,
-                     p.score_keys, (int32_t*)(ws + w.plan), (uint4*)(ws + w.zero_begin), n16);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // K1a: g_t = mean_j unit(q_{t,j}) over the G query heads of KV head h, for a
@@ -86,17 +86,45 @@ __device__ __forceinline__ void load_row(const T* __restrict__ p, float (&x)[EPL
 template <typename T, int D>
 __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ cu_chunk,
-    const int32_t* __restrict__ plan, int S, int Hq, int Hkv, int G, float* __restrict__ g,
-    double* __restrict__ gpart) {
+    const int32_t* __restrict__ cu_hist, int S, int Hq, int Hkv, int G, float* __restrict__ g,
+    double* __restrict__ gpart, int score_keys, int32_t* __restrict__ plan,
+    uint4* __restrict__ zero, int64_t nzero16) {
   constexpr int EPL = D / 16;  // elements per lane
   const int tile = blockIdx.x, h = blockIdx.y;
-  const int32_t* qt_off = plan;
-  const int s = upper_seq(qt_off, S, tile);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the plan and the cleared counters are for the later kernels
+  {
+    const int64_t nb = (int64_t)gridDim.x * gridDim.y;
+    for (int64_t i = ((int64_t)h * gridDim.x + tile) * kQprepThreads + threadIdx.x; i < nzero16;
+         i += nb * kQprepThreads)
+      zero[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (tile == 0 && h == 0 && threadIdx.x == 0) write_plan(cu_chunk, cu_hist, S, score_keys, plan);
+  }
+  // this tile's sequence: wave prefix sums over the sequences' tile counts
+  int s = 0, t_base = 0;
+  for (int s0 = 0, acc = 0; s0 < S; s0 += 64) {
+    const int sq = s0 + lane;
+    const int n = sq < S ? (cu_chunk[sq + 1] - cu_chunk[sq] + kQprepTokens - 1) / kQprepTokens : 0;
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const int excl = incl - n;
+    const uint64_t m = __ballot(n > 0 && acc + excl <= tile && tile < acc + incl);
+    if (m) {
+      const int l = __ffsll((unsigned long long)m) - 1;
+      s = s0 + l;
+      t_base = acc + __shfl(excl, l, 64);
+      break;
+    }
+    acc += __shfl(incl, 63, 64);
+  }
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, sub = lane & 15;
-  const int tw = (tile - qt_off[s]) * kQprepTokens + wave * kTokPerWave;
+  const int tw = (tile - t_base) * kQprepTokens + wave * kTokPerWave;
 
   float acc[kTokPerWave][EPL];
 #pragma unroll
@@ -358,15 +386,22 @@ __global__ __launch_bounds__(kQprepThreads) void qselect_kernel(
 
 hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
                         float* qcos, int32_t* qidx, int32_t* sel_idx, hipStream_t st) {
-  const int32_t* plan = (const int32_t*)(ws + w.plan);
+  int32_t* plan = (int32_t*)(ws + w.plan);
   float* g = (float*)(ws + w.g);
   double* gpart = (double*)(ws + w.gpart);
+  uint4* zero = (uint4*)(ws + w.zero_begin);
+  const int64_t n16 = (int64_t)((w.zero_end - w.zero_begin) / 16);
   const dim3 block(kQprepThreads);
-  if (p.NQT > 0) {
+  if (p.NQT == 0) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, p.cu_chunk, p.cu_hist, p.S,
+                       p.score_keys, plan, zero, n16);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
     dim3 grid((unsigned)p.NQT, (unsigned)p.Hkv);
 #define QUOKA_QPREP(T, D)                                                                     \
   hipLaunchKernelGGL((qprep_g_kernel<T, D>), grid, block, 0, st, (const T*)q, p.cu_chunk,     \
-                     plan, p.S, p.Hq, p.Hkv, p.G, g, gpart)
+                     p.cu_hist, p.S, p.Hq, p.Hkv, p.G, g, gpart, p.score_keys, plan, zero, n16)
     if (p.dtype == QUOKA_BF16) {
       if (p.D == 128) QUOKA_QPREP(bf16, 128); else QUOKA_QPREP(bf16, 64);
     } else {
