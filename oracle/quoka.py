@@ -52,8 +52,11 @@ __all__ = [
     "unit", "cosine_matrix", "group_query", "query_cosines",
     "lowest_cosine_queries", "key_scores", "top_b_keys", "attend_rows",
     "attend_chunk", "select_for_head", "prefill_chunk", "effective_budgets",
-    "prefill_prompt",
+    "prefill_prompt", "VARIANTS", "global_query_cosines", "select_for_sequence",
 ]
+
+# QUOKA and the baselines the pages set it against (see select_for_sequence).
+VARIANTS = ("quoka", "dot", "mean_queries", "mean_query", "per_head", "global")
 
 
 def _f64(x) -> np.ndarray:
@@ -257,10 +260,83 @@ def select_for_head(q_grp, k, n_q: int, budget: int, **score_kw):
     return {"c": c, "S": S, "s": s, "I": I}
 
 
+def global_query_cosines(q_seq, num_kv_heads: int) -> np.ndarray:
+    """One cosine per token for the whole sequence: the mean over the KV heads
+    (in head order) of the per-head cosines c_{t,h} to each head's mean query.
+
+    q_seq: [C, H_q, d] -> [C]. Used by the cross-head ("global") baseline,
+    where one token subset serves every KV head. [EXP] "A wrinkle:
+    grouped-query attention" speaks of one selected token carrying several
+    query-head representations, one group per KV head; the average follows
+    the GQA-axis rule of [SUM] "Aggregation Across Queries and KV Groups".
+    """
+    q_seq = _f64(q_seq)
+    C, H_q = q_seq.shape[0], q_seq.shape[1]
+    H_kv = int(num_kv_heads)
+    G = H_q // H_kv
+    acc = np.zeros((C,), np.float64)
+    for h in range(H_kv):
+        acc = acc + query_cosines(q_seq[:, h * G:(h + 1) * G, :])[2]
+    return acc / H_kv
+
+
+def select_for_sequence(q_seq, k_seq, n_q: int, budget: int, variant: str = "quoka"):
+    """Selection for every KV head of one sequence, by QUOKA or a baseline.
+
+    q_seq [C, H_q, d]; k_seq [L, H_kv, d]. Returns one dict per KV head with
+    c [C] (that head's cosines), S (kept token ids, ascending), s [L], I.
+
+      quoka        the method (select_for_head).
+      per_head     the same scores, which the direct form here already takes
+                   head by head; [EXP] "A wrinkle: grouped-query attention"
+                   names it as the costly way (each head scored, then averaged).
+      dot          scores by raw dot products, max over kept tokens of the mean
+                   over the group's heads ([SUM] "Scoring via Cosine
+                   Similarity": the scale-dependent QK^T of earlier methods).
+      mean_queries mean over kept tokens instead of max ([SUM] "Aggregation
+                   Across Queries and KV Groups", query axis; [EXP] "Why take
+                   the maximum").
+      mean_query   no subselection: every chunk token, averaged, scores the keys
+                   ([SUM] "Background > Attention Sparsity": single-query
+                   methods stretched to many queries by averaging them; [EXP]
+                   "One query can choose for itself, but a chunk has
+                   thousands"). S is empty.
+      global       one kept-token subset per sequence from global_query_cosines,
+                   shared by all KV heads; scoring and top-B stay per head.
+    """
+    if variant not in VARIANTS:
+        raise ValueError(variant)
+    q_seq, k_seq = _f64(q_seq), _f64(k_seq)
+    C, H_q = q_seq.shape[0], q_seq.shape[1]
+    H_kv = k_seq.shape[1]
+    G = H_q // H_kv
+    S_glob = None
+    if variant == "global":
+        S_glob = lowest_cosine_queries(global_query_cosines(q_seq, H_kv), n_q)
+    res = []
+    for h in range(H_kv):
+        q_grp = q_seq[:, h * G:(h + 1) * G, :]
+        k_h = k_seq[:, h, :]
+        if variant in ("quoka", "per_head"):
+            res.append(select_for_head(q_grp, k_h, n_q, budget))
+            continue
+        _, _, c = query_cosines(q_grp)
+        if variant == "mean_query":
+            S = np.zeros((0,), np.int64)
+            s = key_scores(q_grp, k_h, query_agg="mean")
+        else:
+            S = S_glob if variant == "global" else lowest_cosine_queries(c, n_q)
+            kw = {"dot": {"sim": "dot"}, "mean_queries": {"query_agg": "mean"},
+                  "global": {}}[variant]
+            s = key_scores(q_grp[S], k_h, **kw)
+        res.append({"c": c, "S": S, "s": s, "I": top_b_keys(s, budget)})
+    return res
+
+
 def prefill_chunk(q, k_hist, v_hist, k_chunk, v_chunk, cu_chunk, cu_hist,
                   num_kv_heads: int, n_q: int, budget: int,
                   scale: float | None = None, *, heads=None,
-                  attention: bool = True, **score_kw):
+                  attention: bool = True, variant: str | None = None, **score_kw):
     """The whole per-chunk hot path over a batch of ragged sequences.
 
     Layouts (token-major, as the library takes them):
@@ -270,7 +346,9 @@ def prefill_chunk(q, k_hist, v_hist, k_chunk, v_chunk, cu_chunk, cu_hist,
     attention": contiguous groups).
 
     ``heads`` restricts the work to a list of KV heads (other outputs stay at
-    their fill values); ``attention=False`` skips the attention step.
+    their fill values); ``attention=False`` skips the attention step;
+    ``variant`` picks a baseline selection (select_for_sequence) in place of
+    QUOKA's.
 
     returns dict with
       out     [sum C, H_q, d]  float64 (NaN where not computed)
@@ -301,10 +379,16 @@ def prefill_chunk(q, k_hist, v_hist, k_chunk, v_chunk, cu_chunk, cu_hist,
     for sq in range(n_seq):
         c0, c1 = cu_chunk[sq], cu_chunk[sq + 1]
         h0, h1 = cu_hist[sq], cu_hist[sq + 1]
+        per_seq = None
+        if variant is not None:
+            per_seq = select_for_sequence(q[c0:c1], k_hist[h0:h1], n_q, budget, variant)
         for h in heads:
             q_grp = q[c0:c1, h * G:(h + 1) * G, :]
             k_h = k_hist[h0:h1, h, :]
-            r = select_for_head(q_grp, k_h, n_q, budget, **score_kw)
+            if per_seq is not None:
+                r = per_seq[h]
+            else:
+                r = select_for_head(q_grp, k_h, n_q, budget, **score_kw)
             qcos[h, c0:c1] = r["c"]
             scores[h, h0:h1] = r["s"]
             q_idx[sq, h, :r["S"].shape[0]] = r["S"]

@@ -320,6 +320,85 @@ def pin_prompt_chunk_zero_and_single_chunk_ignore_the_budget():
     assert not np.allclose(r["out"][64:], dense[64:])  # later chunks see only 3 history keys
 
 
+# ------------------------------------------------ baselines (select_for_sequence)
+def pin_variant_dot_closed_form():
+    """Raw dot products: max over tokens of the mean over the group's heads."""
+    q = np.array([[[3.0, 4.0], [0.0, 2.0]],      # token 0, heads 0 and 1
+                  [[0.0, -1.0], [1.0, 0.0]]])    # token 1
+    k = np.array([[[1.0, 0.0]], [[0.0, 1.0]], [[2.0, 0.0]]])   # [L=3, H_kv=1, d]
+    r = oracle.select_for_sequence(q, k, 2, 2, "dot")[0]
+    # key 0: means 1.5, 0.5; key 1: 3, -0.5; key 2 (key 0 doubled): 3, 1
+    np.testing.assert_allclose(r["s"], [1.5, 3.0, 3.0], atol=1e-15)
+    assert r["I"].tolist() == [1, 2]
+    r_cos = oracle.select_for_sequence(q, k, 2, 2, "quoka")[0]
+    assert r_cos["s"][0] == pytest.approx(r_cos["s"][2], abs=1e-15)  # cosine ignores scale
+
+
+def pin_variant_mean_queries_worked_example():
+    """The score table of the worked example averaged over its three queries."""
+    ex = GOLD["score_table"]
+    q, k = _table_vectors(ex["cos"])
+    r = oracle.select_for_sequence(q[:, None, :], k[:, None, :], 3, 2, "mean_queries")[0]
+    np.testing.assert_allclose(r["s"][0], ex["mean_over_queries_K1"], atol=1e-14)
+    # the other columns of the printed table, averaged by hand
+    np.testing.assert_allclose(r["s"], [0.40, 0.35, 1.30 / 3, 0.15], atol=1e-14)
+    assert r["S"].tolist() == [0, 1, 2] and r["I"].tolist() == [0, 2]
+
+
+def pin_variant_mean_query_closed_form():
+    """One query, the chunk's mean: tokens e1, e1, e2 (norms 2, 0.5, 7) give
+    per-key mean cosines 2/3 (e1), 1/3 (e2) and 1/sqrt(2) ((e1 + e2) scaled)."""
+    q = np.zeros((3, 1, 4))
+    q[0, 0, 0], q[1, 0, 0], q[2, 0, 1] = 2.0, 0.5, 7.0
+    k = np.zeros((3, 1, 4))
+    k[0, 0, 0], k[1, 0, 1] = 3.0, 1.0
+    k[2, 0, :2] = 5.0
+    r = oracle.select_for_sequence(q, k, 1, 1, "mean_query")[0]
+    np.testing.assert_allclose(r["s"], [2 / 3, 1 / 3, 1 / math.sqrt(2)], atol=1e-15)
+    assert r["S"].shape == (0,) and r["I"].tolist() == [2]
+    # QUOKA with the one kept token (e2, the least like the mean) scores e2 highest
+    rq = oracle.select_for_sequence(q, k, 1, 1, "quoka")[0]
+    assert rq["S"].tolist() == [2] and rq["I"].tolist() == [1]
+
+
+def _two_head_tokens():
+    # head 0: tokens e1 (x2), e1 (x0.5), e2 (x7); head 1: e2, e1, e1 (G = 1)
+    q = np.zeros((3, 2, 4))
+    q[0, 0, 0], q[1, 0, 0], q[2, 0, 1] = 2.0, 0.5, 7.0
+    q[0, 1, 1], q[1, 1, 0], q[2, 1, 0] = 1.0, 3.0, 1.0
+    k = np.zeros((2, 2, 4))
+    k[0, :, 0] = 1.0
+    k[1, :, 1] = 1.0
+    return q, k
+
+
+def pin_variant_global_closed_form():
+    """Per-head cosines (2, 2, 1)/sqrt(5) and (1, 2, 2)/sqrt(5) average to
+    (1.5, 2, 1.5)/sqrt(5); the shared lowest token is 0 (tie to the lower)."""
+    q, k = _two_head_tokens()
+    r5 = math.sqrt(5.0)
+    np.testing.assert_allclose(oracle.global_query_cosines(q, 2),
+                               [1.5 / r5, 2 / r5, 1.5 / r5], atol=1e-15)
+    glob = oracle.select_for_sequence(q, k, 1, 1, "global")
+    per = oracle.select_for_sequence(q, k, 1, 1, "quoka")
+    assert [r["S"].tolist() for r in glob] == [[0], [0]]
+    assert [r["S"].tolist() for r in per] == [[2], [0]]
+    np.testing.assert_allclose(glob[0]["s"], [1.0, 0.0], atol=1e-15)   # token 0 of head 0 is e1
+    np.testing.assert_allclose(per[0]["s"], [0.0, 1.0], atol=1e-15)    # token 2 of head 0 is e2
+    assert [r["S"].tolist() for r in oracle.select_for_sequence(q, k, 2, 1, "global")] == \
+        [[0, 2], [0, 2]]
+
+
+def pin_variant_global_with_one_kv_head_is_quoka():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((9, 3, 8))
+    k = rng.standard_normal((20, 1, 8))
+    a = oracle.select_for_sequence(q, k, 4, 6, "global")[0]
+    b = oracle.select_for_head(q, k[:, 0], 4, 6)
+    assert a["S"].tolist() == b["S"].tolist() and a["I"].tolist() == b["I"].tolist()
+    np.testing.assert_allclose(a["s"], b["s"], atol=1e-15)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -368,6 +447,12 @@ def _mutations():
         i = np.arange(s.shape[0])
         return np.sort(orig_lexsort((-i, -s))[:min(b, s.shape[0])])
 
+    def global_head0(q_seq, num_kv_heads):
+        q_seq = np.asarray(q_seq, np.float64)
+        G = q_seq.shape[1] // num_kv_heads
+        return orig_query_cosines(q_seq[:, :G, :])[2]
+
+    orig_query_cosines = oq.query_cosines
     orig_key_scores, orig_lowest, orig_top = oq.key_scores, oq.lowest_cosine_queries, oq.top_b_keys
     orig_attend = oq.attend_rows
     return {
@@ -380,6 +465,7 @@ def _mutations():
         "tie_to_higher_index": ("top_b_keys", tie_high_index),
         "mask_without_diagonal": ("attend_rows", causal_strict),
         "chunk_mask_without_diagonal": ("attend_chunk", chunk_strict),
+        "global_from_first_head_only": ("global_query_cosines", global_head0),
     }
 
 
