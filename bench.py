@@ -4,7 +4,9 @@ A step is one pass of the whole path (query subselection, key scoring, top-B
 select, K/V gather, chunk attention) over one layer's chunk, all heads, with
 inputs already resident in HBM. By default the gather runs fused into the
 attention (quoka_select, then quoka_chunk_attn_gather); --unfused times the
-three separate calls (quoka_select, quoka_gather, quoka_chunk_attn). Several rotated copies of the inputs are
+three separate calls (quoka_select, quoka_gather, quoka_chunk_attn); --variant
+times one of the pages' baseline selections in place of QUOKA's (then without
+the CPU baseline). Several rotated copies of the inputs are
 cycled through so that consecutive steps do not hit the 256 MB last-level
 cache with the previous step's history keys.
 
@@ -215,6 +217,9 @@ def main():
                     help="time a whole prompt of T tokens through chunked prefill "
                          "(quoka_prefill_prompt) against dense chunked prefill instead")
     ap.add_argument("--chunk", type=int, default=2048, help="chunk length for --prompt")
+    ap.add_argument("--variant", default="quoka",
+                    choices=["quoka", "dot", "mean_queries", "mean_query", "per_head", "global"],
+                    help="time a baseline selection (quoka_select_variant) in place of QUOKA's")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the "
                          "reference for scaling HBM byte counters")
@@ -270,7 +275,8 @@ def main():
         x = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        cpk.select(shape, x["q"], x["k_hist"], w.n_q, B, sel_idx=sel, workspace=ws)
+        cpk.select(shape, x["q"], x["k_hist"], w.n_q, B, sel_idx=sel, workspace=ws,
+                   variant=args.variant)
         if ev is not None:
             ev[1].record()
         if args.unfused:
@@ -327,7 +333,7 @@ def main():
                    "chunk_tokens": int(tokens), "history_tokens": int(TL),
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "q_budget": w.n_q, "kv_budget": B,
-                   "input_sets": len(sets),
+                   "input_sets": len(sets), "selection": args.variant,
                    "path": "select + gather + chunk_attn" if args.unfused
                            else "select + chunk_attn_gather (gather fused)"},
         "stages_us": ({"select": round(sel_us, 2), "gather": round(gat_us, 2),
@@ -344,7 +350,7 @@ def main():
                       {"gather": "fused into the attention (quoka_chunk_attn_gather)"}) |
                      {"scorer_bytes": scorer_bytes(w)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.variant == "quoka":
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
 

@@ -23,8 +23,12 @@ LIB_PATH = os.path.join(_PKG, "lib", "libquoka.so")
 QUOKA_OK, QUOKA_EINVAL, QUOKA_EUNSUPPORTED, QUOKA_EWORKSPACE, QUOKA_EHIP = range(5)
 QUOKA_F32, QUOKA_BF16 = 0, 1
 MAX_Q_BUDGET = 128
+# quoka_variant: QUOKA and the baseline selections the pages compare it with
+VARIANTS = {"quoka": 0, "dot": 1, "mean_queries": 2, "mean_query": 3, "per_head": 4,
+            "global": 5}
 
-SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_gather", "quoka_chunk_attn",
+SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_select_variant", "quoka_gather",
+           "quoka_chunk_attn",
            "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prompt_workspace_bytes",
            "quoka_prefill_prompt", "quoka_strerror", "quoka_last_error")
 
@@ -78,6 +82,7 @@ def load_library(path: str = LIB_PATH):
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.quoka_workspace_bytes.argtypes = [sp, i32, i32, P(sz)]
     lib.quoka_select.argtypes = [sp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.quoka_select_variant.argtypes = [sp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.quoka_gather.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp]
     lib.quoka_chunk_attn.argtypes = [sp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp]
     lib.quoka_chunk_attn_gather.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
@@ -188,9 +193,15 @@ def alloc_workspace(shape: Shape, q_budget: int, kv_budget: int) -> torch.Tensor
 
 
 def select(shape: Shape, q, k_hist, q_budget: int, kv_budget: int, *, sel_idx=None,
-           want_q_idx=False, want_qcos=False, want_scores=False, workspace=None):
-    """Kept history indices per (sequence, KV head); optional stage outputs."""
+           want_q_idx=False, want_qcos=False, want_scores=False, workspace=None,
+           variant: str = "quoka"):
+    """Kept history indices per (sequence, KV head); optional stage outputs.
+
+    ``variant`` other than "quoka" runs a baseline selection
+    (quoka_select_variant; names as in VARIANTS)."""
     lib = load_library()
+    if variant not in VARIANTS:
+        raise ValueError(f"variant {variant!r} is not one of {sorted(VARIANTS)}")
     S, Hq, Hkv, d = shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
     shape._check_tensor(q, "q", (shape.total_chunk, Hq, d), shape.torch_dtype)
     shape._check_tensor(k_hist, "k_hist", (shape.total_hist, Hkv, d), shape.torch_dtype)
@@ -205,9 +216,17 @@ def select(shape: Shape, q, k_hist, q_budget: int, kv_budget: int, *, sel_idx=No
         if want_scores else None
     if workspace is None:
         workspace = alloc_workspace(shape, q_budget, kv_budget)
-    _check(lib.quoka_select(ctypes.byref(shape.c), _ptr(q), _ptr(k_hist), q_budget, kv_budget,
-                            _ptr(sel_idx), _ptr(q_idx), _ptr(qcos), _ptr(scores),
-                            _ptr(workspace), workspace.numel(), _stream(dev)), "quoka_select")
+    if variant == "quoka":
+        _check(lib.quoka_select(ctypes.byref(shape.c), _ptr(q), _ptr(k_hist), q_budget,
+                                kv_budget, _ptr(sel_idx), _ptr(q_idx), _ptr(qcos), _ptr(scores),
+                                _ptr(workspace), workspace.numel(), _stream(dev)),
+               "quoka_select")
+    else:
+        _check(lib.quoka_select_variant(ctypes.byref(shape.c), VARIANTS[variant], _ptr(q),
+                                        _ptr(k_hist), q_budget, kv_budget, _ptr(sel_idx),
+                                        _ptr(q_idx), _ptr(qcos), _ptr(scores), _ptr(workspace),
+                                        workspace.numel(), _stream(dev)),
+               "quoka_select_variant")
     return {"sel_idx": sel_idx, "q_idx": q_idx, "qcos": qcos, "scores": scores}
 
 

@@ -46,27 +46,33 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Largest dynamic LDS the scorer asks for; raised once per device.
+// Largest dynamic LDS the scorer asks for; raised once per device (the
+// per-head baseline's kernels to all the device offers).
 quoka_status ensure_lds(const Problem& p) {
   static std::mutex mu;
-  static bool done[64] = {};
+  static int max_lds[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(QUOKA_EHIP, "hipGetDevice failed");
   if (dev < 0 || dev >= 64) return fail(QUOKA_EUNSUPPORTED, "device ordinal %d", dev);
   std::lock_guard<std::mutex> lock(mu);
-  if (done[dev]) return QUOKA_OK;
-  int max_lds = 0;
-  if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-      hipSuccess)
-    return fail(QUOKA_EHIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed");
-  const int need = kScoreBins * 4 + QUOKA_MAX_Q_BUDGET * 128 * 4;
-  if (max_lds < need)
-    return fail(QUOKA_EUNSUPPORTED, "device offers %d bytes of LDS per workgroup, scorer needs %d",
-                max_lds, need);
-  const hipError_t e = set_scorer_lds_limit(need);
-  if (e != hipSuccess)
-    return fail(QUOKA_EHIP, "hipFuncSetAttribute(scorer LDS): %s", hipGetErrorString(e));
-  done[dev] = true;
+  if (max_lds[dev] == 0) {
+    int lds = 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return fail(QUOKA_EHIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed");
+    const int need = kScoreBins * 4 + QUOKA_MAX_Q_BUDGET * 128 * 4;
+    if (lds < need)
+      return fail(QUOKA_EUNSUPPORTED,
+                  "device offers %d bytes of LDS per workgroup, scorer needs %d", lds, need);
+    const hipError_t e = set_scorer_lds_limit(need, lds);
+    if (e != hipSuccess)
+      return fail(QUOKA_EHIP, "hipFuncSetAttribute(scorer LDS): %s", hipGetErrorString(e));
+    max_lds[dev] = lds;
+  }
+  const size_t want = scorer_lds_bytes(p);
+  if (want > (size_t)max_lds[dev])
+    return fail(QUOKA_EUNSUPPORTED,
+                "the per-head baseline needs %zu bytes of LDS per workgroup, the device offers %d",
+                want, max_lds[dev]);
   return QUOKA_OK;
 }
 
@@ -138,6 +144,22 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
   p->q_budget = q_budget;
   p->kv_budget = kv_budget;
   p->nq_pad = (q_budget + 15) / 16 * 16;
+  p->variant = QUOKA_VARIANT_QUOKA;
+  return QUOKA_OK;
+}
+
+// What a baseline needs beyond make_problem's checks.
+quoka_status set_variant(int32_t variant, Problem* p) {
+  if (variant < QUOKA_VARIANT_QUOKA || variant > QUOKA_VARIANT_GLOBAL)
+    return fail(QUOKA_EINVAL, "variant=%d is not a quoka_variant", variant);
+  p->variant = variant;
+  if (variant == QUOKA_VARIANT_GLOBAL && p->maxC > kQselCap)
+    return fail(QUOKA_EUNSUPPORTED, "the cross-head baseline takes chunks of at most %d tokens",
+                kQselCap);
+  if (variant == QUOKA_VARIANT_PER_HEAD && (int64_t)p->nq_pad * p->G > kMaxHeadRows)
+    return fail(QUOKA_EUNSUPPORTED,
+                "the per-head baseline takes ceil(q_budget/16)*16 * H_q/H_kv <= %d rows",
+                kMaxHeadRows);
   return QUOKA_OK;
 }
 
@@ -157,7 +179,7 @@ Workspace workspace_layout(const Problem& p) {
   w.gpart = take((size_t)p.NQT * p.Hkv * p.D * 8);
   w.qcos = take((size_t)p.Hkv * p.TC * 4);
   w.qidx = take(SH * p.q_budget * 4);
-  w.gsel = take(SH * p.nq_pad * p.D * 4);
+  w.gsel = take(SH * p.nq_pad * p.G * p.D * 4);  // G rows per token: the per-head baseline
   w.scores = take((size_t)p.Hkv * p.TL * 4);
   w.zero_begin = o;
   w.hist = take(SH * kScoreBins * 4);
@@ -222,6 +244,28 @@ quoka_status quoka_select(const quoka_shape* shape, const void* q, const void* k
   Problem p;
   quoka_status rc = make_problem(shape, q_budget, kv_budget, &p);
   if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(q, p.TC);
+  QUOKA_NEED(k_hist, p.TL);
+  QUOKA_NEED(sel_idx, 1);
+  if (!ws) return fail(QUOKA_EWORKSPACE, "workspace is null");
+  if (!aligned16(ws)) return fail(QUOKA_EINVAL, "workspace is not 16-byte aligned");
+  const Workspace w = workspace_layout(p);
+  if (ws_bytes < w.total)
+    return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  return run_select(p, w, q, k_hist, sel_idx, q_idx_opt, qcos_opt, scores_opt, (char*)ws,
+                    stream);
+}
+
+quoka_status quoka_select_variant(const quoka_shape* shape, int32_t variant, const void* q,
+                                  const void* k_hist, int32_t q_budget, int32_t kv_budget,
+                                  int32_t* sel_idx, int32_t* q_idx_opt, float* qcos_opt,
+                                  float* scores_opt, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, q_budget, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  if ((rc = set_variant(variant, &p)) != QUOKA_OK) return rc;
   QUOKA_NEED(q, p.TC);
   QUOKA_NEED(k_hist, p.TL);
   QUOKA_NEED(sel_idx, 1);

@@ -63,6 +63,12 @@ __device__ __forceinline__ int score_bin(float s) {
   return (int)x;
 }
 
+// Histogram bin of an unbounded score (raw dot products): the top 11 bits of
+// its order key. Monotone non-decreasing over all floats; coarse (4 bins per
+// binade), which only makes the top-B refinement see more candidates.
+__device__ __forceinline__ int score_bin_raw(float s) { return (int)(float_order_key(s) >> 21); }
+static_assert(kScoreBins == 2048, "score_bin_raw yields 11 bits");
+
 // ---- buffer loads ----------------------------------------------------------
 // Raw buffer resource over [p, p + nbytes): loads at byte offsets >= nbytes
 // return zeros (bounds checked in hardware on the VGPR offset). p and nbytes

@@ -17,6 +17,14 @@ constexpr int kScoreKeysSmall = 512; // ...or half as many when that fills the C
 constexpr int kScoreMinBlocks = 512; // scorer workgroups wanted (two per CU)
 constexpr int kTopbKeys = 512;       // history keys per top-B workgroup
 constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
+constexpr int kQselCap = 12288;      // chunk tokens whose cosines the query select stages in LDS
+
+// How the scorer forms a key's score from the rows the query select lays out.
+enum ScoreMode {
+  kModeCos = 0,    // max over rows of g . k / |k| (QUOKA and the cosine baselines)
+  kModeDot = 1,    // max over rows of g . k, unbounded (histogram by score_bin_raw)
+  kModeHeads = 2,  // rows hold each head separately: max over tokens of mean over heads
+};
 
 struct Problem {
   int S, Hq, Hkv, G, D;
@@ -30,7 +38,20 @@ struct Problem {
   int maxC, maxL;            // longest chunk, longest history
   int q_budget, kv_budget, nq_pad;
   int score_keys;            // history keys per scorer workgroup (kScoreKeys or kScoreKeysSmall)
+  int variant;               // quoka_variant
+  int mode() const {
+    return variant == QUOKA_VARIANT_DOT ? kModeDot
+         : variant == QUOKA_VARIANT_PER_HEAD ? kModeHeads : kModeCos;
+  }
+  // the scorer reads one row per (sequence, head): the mean-query baselines
+  bool one_row() const {
+    return variant == QUOKA_VARIANT_MEAN_QUERIES || variant == QUOKA_VARIANT_MEAN_QUERY;
+  }
+  int gh() const { return variant == QUOKA_VARIANT_PER_HEAD ? G : 1; }  // rows per kept token
 };
+
+// Largest (kept rows) x (heads) the per-head baseline lays out (LDS-bound).
+constexpr int kMaxHeadRows = 640;
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct Workspace {
@@ -39,7 +60,7 @@ struct Workspace {
   size_t gpart;     // double [NQT, Hkv, D] per-tile sums of g
   size_t qcos;      // float [Hkv, TC]
   size_t qidx;      // int32 [S, Hkv, q_budget]
-  size_t gsel;      // 4 B x [S, Hkv, nq_pad, D]  kept group queries for the scorer
+  size_t gsel;      // 4 B x [S, Hkv, nq_pad, G, D]  kept queries laid out for the scorer
   size_t scores;    // float [Hkv, TL]
   size_t hist;      // uint32 [S, Hkv, kScoreBins]
   size_t thr;       // Threshold [S, Hkv]
@@ -66,12 +87,14 @@ Workspace workspace_layout(const Problem& p);
 // Launchers (enqueue only; return hipGetLastError()).
 // Raise the dynamic-LDS limit of the scorer kernels (they hold the kept
 // queries and a score histogram on chip).
-hipError_t set_scorer_lds_limit(int bytes);
+// bytes_heads is for the per-head baseline's kernels.
+hipError_t set_scorer_lds_limit(int bytes, int bytes_heads);
 
 // Plan and counter clearing, query prep, cosines and the lowest-cosine
 // select; also writes the -1 padding of sel_idx past each problem's B_eff.
 hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
                         float* qcos, int32_t* qidx, int32_t* sel_idx, hipStream_t st);
+size_t scorer_lds_bytes(const Problem& p);
 hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const Workspace& w,
                          float* scores, hipStream_t st);
 hipError_t launch_topb(const Problem& p, char* ws, const Workspace& w, const float* scores,

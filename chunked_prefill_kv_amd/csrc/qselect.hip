@@ -7,6 +7,8 @@
 // (normalised queries are averaged over the KV group before scoring);
 // "QUOKA Explained", "Pick the queries that disagree with the crowd" and
 // "A wrinkle: grouped-query attention".
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "radix.h"
@@ -196,22 +198,14 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
 // ---------------------------------------------------------------------------
 // K2: keep the N_q,eff tokens with the lowest cosine (ties to the lower
 // token) by an exact radix select over the unique keys
-// (order_key(c) << 32 | t), write them ascending, and lay out the kept g rows
-// for the scorer: bf16 hi/lo pairs in MFMA A-operand order, or fp32 rows.
+// (order_key(c) << 32 | t), and write them ascending to out and kept.
+// Returns N_q,eff.
 // ---------------------------------------------------------------------------
-constexpr int kQselCap = 12288;  // chunk tokens whose cosines are staged in LDS
-
-template <int D, bool kMfma>
-__device__ void select_kept_queries(int prob, int h, int Hkv, int c_off, int C, int q_budget,
-                                    int nq_pad, const float* __restrict__ src_g,
-                                    const float* __restrict__ g, int32_t* __restrict__ qidx,
-                                    void* __restrict__ gsel, float* cs,
-                                    RadixScratch<kQprepThreads>& rs, int32_t* kept) {
-  constexpr int NT = kQprepThreads;
+template <int NT>
+__device__ int select_tokens(int C, int q_budget, const float* __restrict__ src, float* cs,
+                             RadixScratch<NT>& rs, int32_t* __restrict__ out, int32_t* kept) {
   const int n = min(q_budget, C);
-  int32_t* out = qidx + (int64_t)prob * q_budget;
-  const float* src = src_g;
-  if (C <= kQselCap) {
+  if (C <= kQselCap && src != cs) {
     block_copy<NT, 4>(cs, src, C);
     src = cs;
   }
@@ -236,40 +230,20 @@ __device__ void select_kept_queries(int prob, int h, int Hkv, int c_off, int C, 
     }
   }
   for (int i = n + threadIdx.x; i < q_budget; i += NT) out[i] = -1;
-  if (n == 0) return;  // empty chunk: the scorer writes zero scores
-  __syncthreads();
+  return n;
+}
 
-  if constexpr (kMfma) {
-    // A operand of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and the
-    // 8 d-values (l/16)*8.. of the 32-wide d-step; layout
-    // [qb][ds][term: hi, lo][lane] of bf16x8. Rows past n repeat row 0,
-    // which leaves the max over kept tokens unchanged.
-    constexpr int NDS = D / 32;
-    bf16x8* dst = (bf16x8*)gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64;
-    const int total = (nq_pad / 16) * NDS * 64;
-    for (int v = threadIdx.x; v < total; v += NT) {
-      const int lane = v & 63, rest = v >> 6;  // rest = qb * NDS + ds
-      const int row = (rest / NDS) * 16 + (lane & 15);
-      const int d0 = (rest % NDS) * 32 + (lane >> 4) * 8;
-      const int t = kept[row < n ? row : 0];
-      const float4* gp = (const float4*)(g + ((int64_t)(c_off + t) * Hkv + h) * D + d0);
-      const float4 x0 = gp[0], x1 = gp[1];
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      bf16x8 hi, lo;
+// 8 consecutive elements of a row as fp32.
+template <typename T>
+__device__ __forceinline__ void load8(const T* __restrict__ p, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 v = *(const bf16x8*)p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = (bf16)x[e];
-        lo[e] = (bf16)(x[e] - (float)hi[e]);
-      }
-      dst[(rest * 2 + 0) * 64 + lane] = hi;
-      dst[(rest * 2 + 1) * 64 + lane] = lo;
-    }
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
   } else {
-    float* dst = (float*)gsel + (int64_t)prob * nq_pad * D;
-    for (int idx = threadIdx.x; idx < n * D; idx += NT) {
-      const int row = idx / D, d = idx % D;
-      dst[idx] = g[((int64_t)(c_off + kept[row]) * Hkv + h) * D + d];
-    }
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
 }
 
@@ -361,27 +335,160 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
   }
 }
 
-// One workgroup per (sequence, KV head): the query select, plus the -1
-// padding of sel_idx past B_eff (the top-B select writes [0, B_eff)).
+// One workgroup per (sequence, KV head): the query select, the -1 padding of
+// sel_idx past B_eff (the top-B select writes [0, B_eff)), and the rows the
+// scorer reads, laid out per variant:
+//   QUOKA, GLOBAL      g_t of the kept tokens
+//   DOT                (1/G) sum_j q_{t,j} of the kept tokens
+//   PER_HEAD           unit(q_{t,j}) for every head j of the kept tokens
+//   MEAN_QUERIES       one row, the mean of the kept tokens' g_t
+//   MEAN_QUERY         one row, the chunk's mean query M (no subselection)
+// bf16 (kMfma): hi/lo bf16 pairs in MFMA A-operand order, 16-row blocks,
+// layout [block][head][d-step][term][lane] of bf16x8; rows past the last
+// repeat row 0 (which leaves a max unchanged). fp32: rows [row][head][d].
 template <int D, bool kMfma>
 __global__ __launch_bounds__(kQprepThreads) void qselect_kernel(
-    const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int Hkv, int64_t TC,
-    const float* __restrict__ g, const float* __restrict__ qcos, int q_budget, int nq_pad,
+    const void* __restrict__ qv, const int32_t* __restrict__ cu_chunk,
+    const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int Hq, int Hkv,
+    int G, int64_t TC, const float* __restrict__ g, const double* __restrict__ gpart,
+    const float* __restrict__ qcos, int q_budget, int nq_pad, int variant,
     int32_t* __restrict__ qidx, void* __restrict__ gsel, int kv_budget,
     int32_t* __restrict__ sel_idx) {
+  using T = typename std::conditional<kMfma, bf16, float>::type;
+  constexpr int NT = kQprepThreads;
+  const T* q = (const T*)qv;
   const int prob = blockIdx.x, s = prob / Hkv, h = prob % Hkv;
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;
   {
     const int L = cu_hist[s + 1] - cu_hist[s];
     int32_t* srow = sel_idx + (int64_t)prob * kv_budget;
-    for (int i = min(kv_budget, L) + threadIdx.x; i < kv_budget; i += kQprepThreads) srow[i] = -1;
+    for (int i = min(kv_budget, L) + threadIdx.x; i < kv_budget; i += NT) srow[i] = -1;
   }
   __shared__ float cs[kQselCap];
   __shared__ int32_t kept[QUOKA_MAX_Q_BUDGET];
-  __shared__ RadixScratch<kQprepThreads> rs;
-  select_kept_queries<D, kMfma>(prob, h, Hkv, c_off, C, q_budget, nq_pad,
-                                qcos + (int64_t)h * TC + c_off, g, qidx, gsel, cs, rs, kept);
+  __shared__ RadixScratch<NT> rs;
+  __shared__ float mrow[D];
+  __shared__ float inv_norm[kMaxHeadRows];
+  int32_t* out = qidx + (int64_t)prob * q_budget;
+  const bool one = variant == QUOKA_VARIANT_MEAN_QUERIES || variant == QUOKA_VARIANT_MEAN_QUERY;
+  const int GH = variant == QUOKA_VARIANT_PER_HEAD ? G : 1;
+
+  int n;
+  if (variant == QUOKA_VARIANT_MEAN_QUERY) {
+    for (int i = threadIdx.x; i < q_budget; i += NT) out[i] = -1;
+    if (C == 0) return;  // the scorer writes zero scores
+    n = 1;
+    if (threadIdx.x < D) {  // M = (1/C) sum of the tile sums, in tile order
+      const int32_t* qt_off = plan;
+      double a = 0.0;
+      for (int k = qt_off[s]; k < qt_off[s + 1]; ++k)
+        a += gpart[((int64_t)k * Hkv + h) * D + threadIdx.x];
+      mrow[threadIdx.x] = (float)(a / (double)C);
+    }
+  } else {
+    const float* src = qcos + (int64_t)h * TC + c_off;
+    if (variant == QUOKA_VARIANT_GLOBAL) {  // C <= kQselCap (checked on the host)
+      for (int t = threadIdx.x; t < C; t += NT) {
+        float a = 0.f;
+        for (int hh = 0; hh < Hkv; ++hh) a += qcos[(int64_t)hh * TC + c_off + t];
+        cs[t] = a / (float)Hkv;
+      }
+      src = cs;
+    }
+    n = select_tokens<NT>(C, q_budget, src, cs, rs, out, kept);
+    if (n == 0) return;  // empty chunk: the scorer writes zero scores
+    __syncthreads();
+    if (variant == QUOKA_VARIANT_MEAN_QUERIES) {
+      if (threadIdx.x < D) {
+        double a = 0.0;
+        for (int r = 0; r < n; ++r)
+          a += (double)g[((int64_t)(c_off + kept[r]) * Hkv + h) * D + threadIdx.x];
+        mrow[threadIdx.x] = (float)(a / (double)n);
+      }
+    } else if (variant == QUOKA_VARIANT_PER_HEAD) {  // n * G <= kMaxHeadRows (host check)
+      for (int i = threadIdx.x; i < n * G; i += NT) {
+        const int r = i / G, j = i % G;
+        const T* row = q + ((int64_t)(c_off + kept[r]) * Hq + (int64_t)h * G + j) * D;
+        float ss = 0.f;
+        for (int d0 = 0; d0 < D; d0 += 8) {
+          float x[8];
+          load8<T>(row + d0, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+        }
+        inv_norm[i] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int nrows = one ? 1 : n;
+  // 8 values (dims d0..d0+7) of row r, head j
+  auto row8 = [&](int r, int j, int d0, float (&x)[8]) {
+    if (one) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = mrow[d0 + e];
+      return;
+    }
+    const int t = c_off + kept[r];
+    if (variant == QUOKA_VARIANT_DOT) {
+      const T* row = q + ((int64_t)t * Hq + (int64_t)h * G) * D + d0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      for (int jj = 0; jj < G; ++jj) {
+        float y[8];
+        load8<T>(row + (int64_t)jj * D, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += y[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] /= (float)G;
+    } else if (variant == QUOKA_VARIANT_PER_HEAD) {
+      load8<T>(q + ((int64_t)t * Hq + (int64_t)h * G + j) * D + d0, x);
+      const float inv = inv_norm[r * G + j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= inv;
+    } else {
+      const float4* gp = (const float4*)(g + ((int64_t)t * Hkv + h) * D + d0);
+      const float4 a = gp[0], b = gp[1];
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+  };
+
+  if constexpr (kMfma) {
+    // A operand of v_mfma_f32_16x16x32_bf16: lane l holds row l%16 and the
+    // 8 d-values (l/16)*8.. of the 32-wide d-step.
+    constexpr int NDS = D / 32;
+    bf16x8* dst = (bf16x8*)gsel + (int64_t)prob * (nq_pad / 16) * GH * NDS * 2 * 64;
+    const int total = (nrows + 15) / 16 * GH * NDS * 64;
+    for (int v = threadIdx.x; v < total; v += NT) {
+      const int lane = v & 63, rest = v >> 6;  // rest = (qb * GH + j) * NDS + ds
+      const int ds = rest % NDS, j = (rest / NDS) % GH, qb = rest / NDS / GH;
+      const int row = qb * 16 + (lane & 15);
+      float x[8];
+      row8(row < nrows ? row : 0, j, ds * 32 + (lane >> 4) * 8, x);
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = (bf16)x[e];
+        lo[e] = (bf16)(x[e] - (float)hi[e]);
+      }
+      dst[(rest * 2 + 0) * 64 + lane] = hi;
+      dst[(rest * 2 + 1) * 64 + lane] = lo;
+    }
+  } else {
+    float* dst = (float*)gsel + (int64_t)prob * nq_pad * GH * D;
+    const int total = nrows * GH * (D / 8);
+    for (int v = threadIdx.x; v < total; v += NT) {
+      const int d0 = (v % (D / 8)) * 8, rj = v / (D / 8);
+      float x[8];
+      row8(rj / GH, rj % GH, d0, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[(int64_t)rj * D + d0 + e] = x[e];
+    }
+  }
 }
 
 hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
@@ -410,7 +517,9 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
 #undef QUOKA_QPREP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.D == 128)
+    if (p.variant == QUOKA_VARIANT_MEAN_QUERY) {
+      // no subselection: the cosines are not needed
+    } else if (p.D == 128)
       hipLaunchKernelGGL((qprep_cos_kernel<128>), grid, block, 0, st, p.cu_chunk, plan, p.S,
                          p.Hkv, p.TC, g, gpart, qcos);
     else
@@ -421,9 +530,9 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
   }
   const dim3 sgrid((unsigned)(p.S * p.Hkv));
 #define QUOKA_QSEL(D, M)                                                                      \
-  hipLaunchKernelGGL((qselect_kernel<D, M>), sgrid, block, 0, st, p.cu_chunk, p.cu_hist, p.Hkv, \
-                     p.TC, g, qcos, p.q_budget, p.nq_pad, qidx, (void*)(ws + w.gsel),         \
-                     p.kv_budget, sel_idx)
+  hipLaunchKernelGGL((qselect_kernel<D, M>), sgrid, block, 0, st, q, p.cu_chunk, p.cu_hist,   \
+                     plan, p.Hq, p.Hkv, p.G, p.TC, g, gpart, qcos, p.q_budget, p.nq_pad,      \
+                     p.variant, qidx, (void*)(ws + w.gsel), p.kv_budget, sel_idx)
   const bool mfma = p.dtype == QUOKA_BF16;
   if (p.D == 128) { if (mfma) QUOKA_QSEL(128, true); else QUOKA_QSEL(128, false); }
   else            { if (mfma) QUOKA_QSEL(64, true);  else QUOKA_QSEL(64, false); }

@@ -9,6 +9,11 @@
 //
 // The epilogue also builds the first-level histogram of the top-B select
 // (linear bins over [-1, 1]) so that the scores are not re-read for it.
+//
+// MODE selects the baselines' arithmetic (kModeDot: no division by |k_i|,
+// histogram over all floats; kModeHeads: each kept token brings G unit head
+// rows, summed per token before the max and divided by G). one_row: the
+// query select laid out a single row (the mean-query baselines).
 #include "common.h"
 #include "internal.h"
 
@@ -36,14 +41,15 @@ __device__ __forceinline__ void flush_hist(const uint32_t* lhist, uint32_t* __re
 // is in flight while the current one is scored. Keys are read through a
 // buffer resource that ends at the sequence's last key, so reads past it
 // return zeros (those keys are never written).
-template <int D, int KEYS>
+template <int D, int KEYS, int MODE>
 __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     const bf16* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int q_budget, int nq_pad, const bf16x8* __restrict__ gsel,
-    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int one_row, int G) {
   constexpr int NDS = D / 32;                 // d-steps per key
   constexpr int NIT = KEYS / 256;             // 64-key blocks per wave
+  const int GH = MODE == kModeHeads ? G : 1;  // rows per kept token
   const int blk = blockIdx.x, h = blockIdx.y;
   const int32_t* sb_off = plan + (S + 1);
   const int s = upper_seq(sb_off, S, blk);
@@ -51,7 +57,7 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
   const int h_off = cu_hist[s];
   const int L = cu_hist[s + 1] - h_off;
   const int k_end = min(L, k_begin + KEYS);
-  const int n = min(q_budget, cu_chunk[s + 1] - cu_chunk[s]);
+  const int n = min(one_row ? 1 : q_budget, cu_chunk[s + 1] - cu_chunk[s]);
   const int nqb = (n + 15) / 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -78,7 +84,8 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
   uint32_t* lhist = (uint32_t*)smem;                       // kScoreBins
   bf16x8* lg = (bf16x8*)(smem + kScoreBins * 4);           // nqb * NDS * 2 * 64
   for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
-  block_copy<256, 8>(lg, gsel + (int64_t)prob * (nq_pad / 16) * NDS * 2 * 64, nqb * NDS * 2 * 64);
+  block_copy<256, 8>(lg, gsel + (int64_t)prob * (nq_pad / 16) * GH * NDS * 2 * 64,
+                     nqb * GH * NDS * 2 * 64);
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;
@@ -89,9 +96,9 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     const int k0 = k_begin + it * 256 + wave * 64;
     if (it + 1 < NIT && k0 + 256 < k_end) load(it + 1, nxt);
     if (k0 >= k_end) break;
-    float nsq[4];
+    float nsq[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 4 && MODE != kModeDot; ++kb) {
       float ss = 0.f;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds)
@@ -109,16 +116,19 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
       f32x4 acc[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) acc[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < GH; ++j) {  // per head rows accumulate: the sum over heads
+        const bf16x8* la = lg + (qb * GH + j) * NDS * 2 * 64 + lane;
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8 ahi = lg[((qb * NDS + ds) * 2 + 0) * 64 + lane];
-        const bf16x8 alo = lg[((qb * NDS + ds) * 2 + 1) * 64 + lane];
+        for (int ds = 0; ds < NDS; ++ds) {
+          const bf16x8 ahi = la[(ds * 2 + 0) * 64];
+          const bf16x8 alo = la[(ds * 2 + 1) * 64];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, cur[kb][ds], acc[kb], 0, 0, 0);
+          for (int kb = 0; kb < 4; ++kb)
+            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, cur[kb][ds], acc[kb], 0, 0, 0);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, cur[kb][ds], acc[kb], 0, 0, 0);
+          for (int kb = 0; kb < 4; ++kb)
+            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, cur[kb][ds], acc[kb], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -135,9 +145,12 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     const float ns = kb == 0 ? nsq[0] : kb == 1 ? nsq[1] : kb == 2 ? nsq[2] : nsq[3];
     const int key = k0 + lane;
     if (key < k_end) {
-      const float sc = (n > 0 && ns > 0.f) ? mm / sqrtf(ns) : 0.f;
+      float sc;
+      if constexpr (MODE == kModeDot) sc = n > 0 ? mm : 0.f;
+      else if constexpr (MODE == kModeHeads) sc = (n > 0 && ns > 0.f) ? mm / ((float)G * sqrtf(ns)) : 0.f;
+      else sc = (n > 0 && ns > 0.f) ? mm / sqrtf(ns) : 0.f;
       srow[key] = sc;
-      atomicAdd(&lhist[score_bin(sc)], 1u);
+      atomicAdd(&lhist[MODE == kModeDot ? score_bin_raw(sc) : score_bin(sc)], 1u);
     }
   }
   __syncthreads();
@@ -146,12 +159,13 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
 
 // fp32 keys (and any dtype as a reference path): one key per thread, kept
 // queries as fp32 rows in LDS read by broadcast.
-template <typename T, int D>
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void scorer_valu_kernel(
     const T* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int q_budget, int nq_pad, const float* __restrict__ gsel,
-    float* __restrict__ scores, uint32_t* __restrict__ hist, int score_keys) {
+    float* __restrict__ scores, uint32_t* __restrict__ hist, int score_keys, int one_row, int G) {
+  const int GH = MODE == kModeHeads ? G : 1;
   const int blk = blockIdx.x, h = blockIdx.y;
   const int32_t* sb_off = plan + (S + 1);
   const int s = upper_seq(sb_off, S, blk);
@@ -159,14 +173,14 @@ __global__ __launch_bounds__(256) void scorer_valu_kernel(
   const int h_off = cu_hist[s];
   const int L = cu_hist[s + 1] - h_off;
   const int k_end = min(L, k_begin + score_keys);
-  const int n = min(q_budget, cu_chunk[s + 1] - cu_chunk[s]);
+  const int n = min(one_row ? 1 : q_budget, cu_chunk[s + 1] - cu_chunk[s]);
   const int prob = s * Hkv + h;
 
   extern __shared__ char smem[];
   uint32_t* lhist = (uint32_t*)smem;
-  float* lg = (float*)(smem + kScoreBins * 4);  // n x D
+  float* lg = (float*)(smem + kScoreBins * 4);  // n x GH x D
   for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
-  block_copy<256, 8>(lg, gsel + (int64_t)prob * nq_pad * D, n * D);
+  block_copy<256, 8>(lg, gsel + (int64_t)prob * nq_pad * GH * D, n * GH * D);
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;
@@ -181,32 +195,63 @@ __global__ __launch_bounds__(256) void scorer_valu_kernel(
     }
     float m = -INFINITY;
     for (int r = 0; r < n; ++r) {
-      const float* gr = lg + r * D;
-      float dot = 0.f;
+      float tot = 0.f;
+      for (int j = 0; j < GH; ++j) {  // per head rows: the sum over heads
+        const float* gr = lg + (r * GH + j) * D;
+        float dot = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) dot = fmaf(gr[d], k[d], dot);
-      m = fmaxf(m, dot);
+        for (int d = 0; d < D; ++d) dot = fmaf(gr[d], k[d], dot);
+        tot += dot;
+      }
+      m = fmaxf(m, tot);
     }
-    const float sc = (n > 0 && ss > 0.f) ? m / sqrtf(ss) : 0.f;
+    float sc;
+    if constexpr (MODE == kModeDot) sc = n > 0 ? m : 0.f;
+    else if constexpr (MODE == kModeHeads) sc = (n > 0 && ss > 0.f) ? m / ((float)G * sqrtf(ss)) : 0.f;
+    else sc = (n > 0 && ss > 0.f) ? m / sqrtf(ss) : 0.f;
     srow[key] = sc;
-    atomicAdd(&lhist[score_bin(sc)], 1u);
+    atomicAdd(&lhist[MODE == kModeDot ? score_bin_raw(sc) : score_bin(sc)], 1u);
   }
   __syncthreads();
   flush_hist(lhist, hist, prob);
 }
 
-hipError_t set_scorer_lds_limit(int bytes) {
-  const void* fns[] = {(const void*)scorer_mfma_kernel<128, kScoreKeys>,
-                       (const void*)scorer_mfma_kernel<64, kScoreKeys>,
-                       (const void*)scorer_mfma_kernel<128, kScoreKeysSmall>,
-                       (const void*)scorer_mfma_kernel<64, kScoreKeysSmall>,
-                       (const void*)scorer_valu_kernel<float, 128>,
-                       (const void*)scorer_valu_kernel<float, 64>};
+hipError_t set_scorer_lds_limit(int bytes, int bytes_heads) {
+  const void* fns[] = {
+      (const void*)scorer_mfma_kernel<128, kScoreKeys, kModeCos>,
+      (const void*)scorer_mfma_kernel<64, kScoreKeys, kModeCos>,
+      (const void*)scorer_mfma_kernel<128, kScoreKeysSmall, kModeCos>,
+      (const void*)scorer_mfma_kernel<64, kScoreKeysSmall, kModeCos>,
+      (const void*)scorer_mfma_kernel<128, kScoreKeys, kModeDot>,
+      (const void*)scorer_mfma_kernel<64, kScoreKeys, kModeDot>,
+      (const void*)scorer_mfma_kernel<128, kScoreKeysSmall, kModeDot>,
+      (const void*)scorer_mfma_kernel<64, kScoreKeysSmall, kModeDot>,
+      (const void*)scorer_valu_kernel<float, 128, kModeCos>,
+      (const void*)scorer_valu_kernel<float, 64, kModeCos>,
+      (const void*)scorer_valu_kernel<float, 128, kModeDot>,
+      (const void*)scorer_valu_kernel<float, 64, kModeDot>};
   for (const void* f : fns) {
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
   }
+  const void* fh[] = {(const void*)scorer_mfma_kernel<128, kScoreKeys, kModeHeads>,
+                      (const void*)scorer_mfma_kernel<64, kScoreKeys, kModeHeads>,
+                      (const void*)scorer_mfma_kernel<128, kScoreKeysSmall, kModeHeads>,
+                      (const void*)scorer_mfma_kernel<64, kScoreKeysSmall, kModeHeads>,
+                      (const void*)scorer_valu_kernel<float, 128, kModeHeads>,
+                      (const void*)scorer_valu_kernel<float, 64, kModeHeads>};
+  for (const void* f : fh) {
+    const hipError_t e =
+        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes_heads);
+    if (e != hipSuccess) return e;
+  }
   return hipSuccess;
+}
+
+// Dynamic LDS of one scorer workgroup: histogram plus the rows it reads.
+size_t scorer_lds_bytes(const Problem& p) {
+  const int rows = p.dtype == QUOKA_BF16 ? p.nq_pad : p.q_budget;
+  return (size_t)kScoreBins * 4 + (size_t)rows * p.gh() * p.D * 4;
 }
 
 hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const Workspace& w,
@@ -215,28 +260,45 @@ hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const W
   dim3 grid((unsigned)p.NSB, (unsigned)p.Hkv);
   const int32_t* plan = (const int32_t*)(ws + w.plan);
   uint32_t* hist = (uint32_t*)(ws + w.hist);
+  const size_t lds = scorer_lds_bytes(p);
+  const int one = p.one_row() ? 1 : 0;
+  const int mode = p.mode();
   if (p.dtype == QUOKA_BF16) {
-    const size_t lds = kScoreBins * 4 + (size_t)p.nq_pad * p.D * 4;
     const bf16x8* gsel = (const bf16x8*)(ws + w.gsel);
     const bool small = p.score_keys == kScoreKeysSmall;
-#define QUOKA_SCORER(D, K)                                                                    \
-  hipLaunchKernelGGL((scorer_mfma_kernel<D, K>), grid, dim3(256), lds, st, (const bf16*)k_hist, \
-                     p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL, p.q_budget, p.nq_pad,     \
-                     gsel, scores, hist)
-    if (p.D == 128) { if (small) QUOKA_SCORER(128, kScoreKeysSmall); else QUOKA_SCORER(128, kScoreKeys); }
-    else            { if (small) QUOKA_SCORER(64, kScoreKeysSmall);  else QUOKA_SCORER(64, kScoreKeys); }
+#define QUOKA_SCORER(D, K, M)                                                                 \
+  hipLaunchKernelGGL((scorer_mfma_kernel<D, K, M>), grid, dim3(256), lds, st,                 \
+                     (const bf16*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,      \
+                     p.q_budget, p.nq_pad, gsel, scores, hist, one, p.G)
+#define QUOKA_SCORER_K(D, M)                                                                  \
+  do {                                                                                        \
+    if (small) QUOKA_SCORER(D, kScoreKeysSmall, M); else QUOKA_SCORER(D, kScoreKeys, M);      \
+  } while (0)
+#define QUOKA_SCORER_M(D)                                                                     \
+  do {                                                                                        \
+    if (mode == kModeDot) QUOKA_SCORER_K(D, kModeDot);                                        \
+    else if (mode == kModeHeads) QUOKA_SCORER_K(D, kModeHeads);                               \
+    else QUOKA_SCORER_K(D, kModeCos);                                                         \
+  } while (0)
+    if (p.D == 128) QUOKA_SCORER_M(128); else QUOKA_SCORER_M(64);
+#undef QUOKA_SCORER_M
+#undef QUOKA_SCORER_K
 #undef QUOKA_SCORER
   } else {
-    const size_t lds = kScoreBins * 4 + (size_t)p.q_budget * p.D * 4;
     const float* gsel = (const float*)(ws + w.gsel);
-    if (p.D == 128)
-      hipLaunchKernelGGL((scorer_valu_kernel<float, 128>), grid, dim3(256), lds, st,
-                         (const float*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,
-                         p.q_budget, p.nq_pad, gsel, scores, hist, p.score_keys);
-    else
-      hipLaunchKernelGGL((scorer_valu_kernel<float, 64>), grid, dim3(256), lds, st,
-                         (const float*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,
-                         p.q_budget, p.nq_pad, gsel, scores, hist, p.score_keys);
+#define QUOKA_SCORER(D, M)                                                                    \
+  hipLaunchKernelGGL((scorer_valu_kernel<float, D, M>), grid, dim3(256), lds, st,             \
+                     (const float*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,     \
+                     p.q_budget, p.nq_pad, gsel, scores, hist, p.score_keys, one, p.G)
+#define QUOKA_SCORER_M(D)                                                                     \
+  do {                                                                                        \
+    if (mode == kModeDot) QUOKA_SCORER(D, kModeDot);                                          \
+    else if (mode == kModeHeads) QUOKA_SCORER(D, kModeHeads);                                 \
+    else QUOKA_SCORER(D, kModeCos);                                                           \
+  } while (0)
+    if (p.D == 128) QUOKA_SCORER_M(128); else QUOKA_SCORER_M(64);
+#undef QUOKA_SCORER_M
+#undef QUOKA_SCORER
   }
   return hipGetLastError();
 }

@@ -23,9 +23,17 @@ __device__ __forceinline__ uint64_t cand_key(float sc, int key) {
   return ((uint64_t)float_order_key(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)key);
 }
 
+// The histogram's bin function: linear over [-1, 1], or over all floats for
+// the unbounded dot-product scores (kRaw).
+template <bool kRaw>
+__device__ __forceinline__ int bin_of(float s) {
+  return kRaw ? score_bin_raw(s) : score_bin(s);
+}
+
 // Keys above the threshold bin b* are counted per tile; keys inside b* are
 // appended to the problem's candidate list (one global atomic per workgroup).
 // Tile 0 of each problem records b* for the later launches.
+template <bool kRaw>
 __global__ __launch_bounds__(256) void topb_filter_kernel(
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int64_t NKT, const float* __restrict__ scores, Threshold* __restrict__ thr,
@@ -61,7 +69,7 @@ __global__ __launch_bounds__(256) void topb_filter_kernel(
   for (int i = 0; i < PER; ++i) {
     const int key = k0 + i * 256 + threadIdx.x;
     const bool ok = key < L;
-    const int bin = score_bin(sc[i]);
+    const int bin = bin_of<kRaw>(sc[i]);
     gt += (ok && bin > t.bstar);
     bal[i] = __ballot(ok && bin == t.bstar);
     nc += (uint32_t)__popcll(bal[i]);
@@ -128,6 +136,7 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(
   }
 }
 
+template <bool kRaw>
 __global__ __launch_bounds__(256) void topb_write_kernel(
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int64_t NKT, int kv_budget, const float* __restrict__ scores,
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(256) void topb_write_kernel(
     const int key = k0 + e;
     if (key < L) {
       const float sc = srow[key];
-      const int bin = score_bin(sc);
+      const int bin = bin_of<kRaw>(sc);
       const bool sel = bin > t.bstar ||
                        (bin == t.bstar && radix_taken<true>(cand_key(sc, key), t.prefix, t.mask));
       flags |= (uint32_t)sel << e;
@@ -182,15 +191,25 @@ hipError_t launch_topb(const Problem& p, char* ws, const Workspace& w, const flo
   uint32_t* gtc = (uint32_t*)(ws + w.gtcount);
   uint32_t* chc = (uint32_t*)(ws + w.chcount);
   const dim3 grid((unsigned)p.NKT, (unsigned)p.Hkv);
-  hipLaunchKernelGGL(topb_filter_kernel, grid, dim3(256), 0, st, p.cu_hist, plan, p.S, p.Hkv, p.TL,
-                     p.NKT, scores, thr, ccount, cand, gtc,
-                     (const uint32_t*)(ws + w.hist), p.kv_budget);
+  const bool raw = p.mode() == kModeDot;
+  if (raw)
+    hipLaunchKernelGGL(topb_filter_kernel<true>, grid, dim3(256), 0, st, p.cu_hist, plan, p.S,
+                       p.Hkv, p.TL, p.NKT, scores, thr, ccount, cand, gtc,
+                       (const uint32_t*)(ws + w.hist), p.kv_budget);
+  else
+    hipLaunchKernelGGL(topb_filter_kernel<false>, grid, dim3(256), 0, st, p.cu_hist, plan, p.S,
+                       p.Hkv, p.TL, p.NKT, scores, thr, ccount, cand, gtc,
+                       (const uint32_t*)(ws + w.hist), p.kv_budget);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topb_cands_kernel, dim3((unsigned)(p.S * p.Hkv)), dim3(256), 0, st, p.cu_hist,
                      plan, p.S, p.Hkv, p.TL, p.NKT, thr, ccount, cand, chc);
-  hipLaunchKernelGGL(topb_write_kernel, grid, dim3(256), 0, st, p.cu_hist, plan, p.S, p.Hkv, p.TL,
-                     p.NKT, p.kv_budget, scores, thr, gtc, chc, sel_idx);
+  if (raw)
+    hipLaunchKernelGGL(topb_write_kernel<true>, grid, dim3(256), 0, st, p.cu_hist, plan, p.S,
+                       p.Hkv, p.TL, p.NKT, p.kv_budget, scores, thr, gtc, chc, sel_idx);
+  else
+    hipLaunchKernelGGL(topb_write_kernel<false>, grid, dim3(256), 0, st, p.cu_hist, plan, p.S,
+                       p.Hkv, p.TL, p.NKT, p.kv_budget, scores, thr, gtc, chc, sel_idx);
   return hipGetLastError();
 }
 

@@ -119,6 +119,51 @@ quoka_status quoka_select(const quoka_shape* shape, const void* q,
                           float* scores_opt, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Baseline selections the pages set QUOKA against, for speed and parity
+ * comparisons (the pages' accuracy claims for them need benchmark data).
+ * Each replaces one step of the selection; everything else is as in
+ * quoka_select. */
+typedef enum quoka_variant {
+  /* QUOKA itself (quoka_select). */
+  QUOKA_VARIANT_QUOKA = 0,
+  /* Key scores by raw dot products: s_i = max over kept tokens t of the mean
+   * over the group's heads j of q_{t,j} . k_i; no normalisation ("QUOKA
+   * Method > Scoring via Cosine Similarity": the scale-dependent QK^T of
+   * earlier methods). The subselection still ranks by cosine. */
+  QUOKA_VARIANT_DOT = 1,
+  /* Mean, not max, over the kept tokens ("Aggregation Across Queries and KV
+   * Groups", query axis; "QUOKA Explained", "Why take the maximum"). */
+  QUOKA_VARIANT_MEAN_QUERIES = 2,
+  /* No subselection: the chunk's mean query M (mean of every token's g_t)
+   * scores the keys, s_i = M . k_i / |k_i| ("Background > Attention
+   * Sparsity": single-query methods stretched to many queries by averaging;
+   * "QUOKA Explained", "One query can choose for itself, but a chunk has
+   * thousands"). q_idx_opt is all -1; qcos_opt is not written. */
+  QUOKA_VARIANT_MEAN_QUERY = 3,
+  /* Scores each kept token's G query heads separately against the keys and
+   * averages afterwards (G times the products; "QUOKA Explained", "A wrinkle:
+   * grouped-query attention"). Same scores as QUOKA up to rounding. Needs
+   * 16 * ceil(q_budget / 16) * H_q / H_kv * head_dim * 4 + 8192 bytes of LDS
+   * per workgroup; QUOKA_EUNSUPPORTED beyond the device's limit. */
+  QUOKA_VARIANT_PER_HEAD = 4,
+  /* One kept-token subset per sequence, shared by all KV heads: the N_q
+   * tokens with the lowest mean over KV heads of the per-head cosines ("QUOKA
+   * Explained", "A wrinkle: grouped-query attention": one selected token,
+   * one query group per KV head). Scoring and top-B stay per KV head. Needs
+   * every chunk to hold at most 12288 tokens (else QUOKA_EUNSUPPORTED). */
+  QUOKA_VARIANT_GLOBAL = 5
+} quoka_variant;
+
+/* quoka_select with the selection of `variant` (a quoka_variant); same
+ * arguments, layouts, workspace size and errors, plus QUOKA_EINVAL for an
+ * unknown variant. */
+quoka_status quoka_select_variant(const quoka_shape* shape, int32_t variant,
+                                  const void* q, const void* k_hist,
+                                  int32_t q_budget, int32_t kv_budget,
+                                  int32_t* sel_idx, int32_t* q_idx_opt,
+                                  float* qcos_opt, float* scores_opt, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /* Gather: step 3 ("QUOKA Explained", "From scores to a smaller KV set": a kept
  * key brings its value). Row b of (s, h) in k_sel / v_sel is row
  * sel_idx[s, h, b] of sequence s, head h of k_hist / v_hist; rows whose index

@@ -111,6 +111,8 @@ def query_cosines(q_grp):
     compute the chunk's mean query, then each query's cosine to it.
     """
     g = group_query(q_grp)
+    if g.shape[0] == 0:  # an empty chunk: no tokens, no mean query
+        return g, np.zeros(g.shape[1:]), np.zeros((0,))
     m = np.mean(g, axis=0)
     c = (unit(g) @ unit(m[None, :]).T)[:, 0]
     return g, m, c

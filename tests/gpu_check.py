@@ -203,3 +203,89 @@ def check_needles(w, r):
             assert pos in kept_k, f"needle seq {s} head {h} key {pos} (token {tok}) missed"
         hit += pos in kept_k
     return hit, len(w.needles), in_s
+
+
+def run_variant(w, shape, t, variant):
+    """Selection by a baseline, with every optional output."""
+    sel = cpk.select(shape, t["q"], t["k_hist"], w.n_q, w.budget, want_q_idx=True,
+                     want_qcos=True, want_scores=True, variant=variant)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in sel.items() if v is not None}
+
+
+def check_variant_selection(w, r, variant):
+    """A baseline's selection, stage-conditioned as check_selection.
+
+    Kept queries: per-head cosines as QUOKA (none for mean_query, whose q_idx
+    is all -1); for global, the oracle's head-averaged cosines and one subset
+    shared by every head. Scores: the oracle's baseline scores on the GPU's
+    kept queries (dot products: error bound relative to |qbar| |k|). Kept keys:
+    the top-B rule on the GPU's scores, bit-exact, and the oracle's within the
+    tie band. Returns tie counts."""
+    q = w.q.astype(np.float64)
+    kh = w.k_hist.astype(np.float64)
+    Hkv = w.num_kv_heads
+    G = w.num_q_heads // Hkv
+    ties = {"q": 0, "k": 0}
+    for s in range(w.num_seqs):
+        c0, c1 = int(w.cu_chunk[s]), int(w.cu_chunk[s + 1])
+        h0, h1 = int(w.cu_hist[s]), int(w.cu_hist[s + 1])
+        nq_eff, b_eff = oracle.effective_budgets(c1 - c0, h1 - h0, w.n_q, w.budget)
+        if variant == "global" and c1 > c0:
+            cg_or = oracle.global_query_cosines(q[c0:c1], Hkv)
+            S_glob = oracle.lowest_cosine_queries(cg_or, w.n_q)
+        for h in range(Hkv):
+            where = f"{variant} seq {s} head {h}"
+            q_grp = q[c0:c1, h * G:(h + 1) * G]
+            qi = r["q_idx"][s, h]
+            if variant == "mean_query":
+                assert np.all(qi == -1), f"{where}: q_idx must be all -1"
+                S_gpu = np.arange(c1 - c0)
+            else:
+                assert np.all(qi[nq_eff:] == -1), f"{where}: q_idx padding"
+                S_gpu = qi[:nq_eff].astype(np.int64)
+                c_gpu = r["qcos"][h, c0:c1].astype(np.float64)
+                if c1 > c0:
+                    _, _, c_or = oracle.query_cosines(q_grp)
+                    err = np.max(np.abs(c_gpu - c_or))
+                    assert err <= QCOS_TOL, f"{where}: qcos error {err:.3g}"
+                if variant == "global":
+                    assert np.array_equal(qi, r["q_idx"][s, 0]), f"{where}: subset not shared"
+                    if c1 > c0:
+                        bound = np.sort(cg_or)[nq_eff - 1]
+                        ties["q"] += _band_check(S_gpu, S_glob, cg_or, bound, QCOS_BAND,
+                                                 f"{where} q_idx")
+                else:
+                    _rule_check(S_gpu, oracle.lowest_cosine_queries(c_gpu, w.n_q),
+                                f"{where} q_idx")
+                    if c1 > c0:
+                        S_or = oracle.lowest_cosine_queries(c_or, w.n_q)
+                        bound = np.sort(c_or)[nq_eff - 1]
+                        ties["q"] += _band_check(S_gpu, S_or, c_or, bound, QCOS_BAND,
+                                                 f"{where} q_idx")
+            s_gpu = r["scores"][h, h0:h1].astype(np.float64)
+            k_h = kh[h0:h1, h]
+            tol = np.full(h1 - h0, SCORE_TOL[w.dtype])
+            if variant == "dot":
+                s_or = oracle.key_scores(q_grp[S_gpu], k_h, sim="dot")
+                if c1 > c0 and h1 > h0:
+                    qbar = np.max(np.linalg.norm(q_grp[S_gpu].mean(axis=1), axis=-1))
+                    tol = 1e-5 * qbar * np.linalg.norm(k_h, axis=-1) + 1e-6
+            elif variant in ("mean_queries", "mean_query"):
+                s_or = oracle.key_scores(q_grp[S_gpu], k_h, query_agg="mean")
+            else:
+                s_or = oracle.key_scores(q_grp[S_gpu], k_h)
+            if h1 > h0:
+                err = np.abs(s_gpu - s_or)
+                assert np.all(err <= tol), \
+                    f"{where}: score error {np.max(err):.3g} (bound {np.min(tol):.3g}..)"
+            si = r["sel_idx"][s, h]
+            assert np.all(si[b_eff:] == -1), f"{where}: sel_idx padding"
+            I_gpu = si[:b_eff].astype(np.int64)
+            _rule_check(I_gpu, oracle.top_b_keys(s_gpu, w.budget), f"{where} sel_idx")
+            if h1 > h0:
+                I_or = oracle.top_b_keys(s_or, w.budget)
+                sb = np.sort(s_or)[::-1][b_eff - 1]
+                band = max(SEL_REL_BAND * abs(sb), 2 * float(np.max(tol)))
+                ties["k"] += _band_check(I_gpu, I_or, s_or, sb, band, f"{where} sel_idx")
+    return ties

@@ -124,3 +124,19 @@ def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(cpk, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         cpk.load_library(str(tmp_path / "missing.so"))
+
+
+@pytest.mark.parametrize("variant,cu_chunk,hq,qb,code,msg", [
+    (9, [0, 10], 8, 8, cpk.QUOKA_EINVAL, "variant"),
+    (-1, [0, 10], 8, 8, cpk.QUOKA_EINVAL, "variant"),
+    (cpk.VARIANTS["global"], [0, 12289], 8, 8, cpk.QUOKA_EUNSUPPORTED, "cross-head"),
+    (cpk.VARIANTS["per_head"], [0, 10], 14, 128, cpk.QUOKA_EUNSUPPORTED, "per-head"),
+])
+def test_select_variant_validation(lib, variant, cu_chunk, hq, qb, code, msg):
+    """Baseline limits are checked on the host, before the workspace or any launch."""
+    shape = _host_shape(cu_chunk, [0, 20], hq=hq)
+    buf = np.zeros(4096, np.uint8)
+    p = buf.ctypes.data + (16 - buf.ctypes.data % 16) % 16
+    st = lib.quoka_select_variant(ctypes.byref(shape.c), variant, p, p, qb, 8, p, None, None,
+                                  None, None, 0, None)
+    assert st == code and msg in lib.quoka_last_error().decode()
