@@ -188,7 +188,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_sel, const bf16* __restrict__ v_sel,
     const int32_t* __restrict__ sel, const bf16* __restrict__ k_chunk, const bf16* __restrict__ v_chunk,
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int S, int Hq,
-    int Hkv, int G, int kv_budget, int ntile_max, float scale_log2, bf16* __restrict__ out) {
+    int Hkv, int G, int kv_budget, int ntile_max, int pair_order, float scale_log2,
+    bf16* __restrict__ out) {
   using TT = AttnTile<D, NW>;
   constexpr int KT = TT::KT, NDS = D / 16, NDB = D / 32;
   constexpr int kAttnRows = TT::ROWS;
@@ -210,7 +211,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   const int rows = C * G;
   const int ntile = (rows + kAttnRows - 1) / kAttnRows;
   if (bx >= ntile) return;
-  const int tile = ntile - 1 - bx;  // longest rows first
+  // Longest rows (most keys) first. When every workgroup is resident at once
+  // (pair_order), the first and second halves of the order fill a CU's two
+  // slots, so the second half runs from light to heavy: each CU then pairs a
+  // heavy tile with a light one instead of two of similar weight.
+  const int half = (ntile + 1) / 2;
+  const int tile = (pair_order && bx >= half) ? bx - half : ntile - 1 - bx;
   const int h_off = cu_hist[s];
   const int Lh = cu_hist[s + 1] - h_off;
   const int B_eff = min(kv_budget, Lh);
@@ -430,6 +436,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
 // half as many of them; they are used when that still leaves two per CU
 // (with one per CU, the causal spread of work between tiles is exposed).
 constexpr int kAttnWideMinBlocks = 512;
+// Four-wave workgroups resident at once on the chip: two per CU (LDS and
+// registers), 256 CUs.
+constexpr int kAttnResident4 = 2 * 256;
 
 hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
                             const void* v_sel, const int32_t* sel, const void* k_chunk,
@@ -442,11 +451,15 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
     const int nw = wide ? 8 : 4;
     const int ntile = (int)((rows + nw * 32 - 1) / (nw * 32));
     dim3 grid((unsigned)(ntile * p.Hkv * p.S));
+    // pair heavy and light tiles when the whole grid is resident: an XCD's
+    // CUs take their first and second workgroups from the first and second
+    // halves of its share of the order
+    const int pair = (!wide && (int64_t)ntile * p.Hkv * p.S <= kAttnResident4) ? 1 : 0;
 #define QUOKA_ATTN(D, NW, IDX)                                                                 \
   hipLaunchKernelGGL((attn_mfma_kernel<D, NW, IDX>), grid, dim3(NW * 64), 0, st, (const bf16*)q, \
                      (const bf16*)k_sel, (const bf16*)v_sel, sel, (const bf16*)k_chunk,           \
                      (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,          \
-                     p.kv_budget, ntile, sl2, (bf16*)out)
+                     p.kv_budget, ntile, pair, sl2, (bf16*)out)
 #define QUOKA_ATTN_NW(D, IDX) { if (wide) QUOKA_ATTN(D, 8, IDX); else QUOKA_ATTN(D, 4, IDX); }
     if (sel) { if (p.D == 128) QUOKA_ATTN_NW(128, true) else QUOKA_ATTN_NW(64, true) }
     else     { if (p.D == 128) QUOKA_ATTN_NW(128, false) else QUOKA_ATTN_NW(64, false) }

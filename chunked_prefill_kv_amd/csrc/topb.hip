@@ -48,10 +48,8 @@ __global__ __launch_bounds__(256) void topb_filter_kernel(
   const int h_off = cu_hist[s];
   const int L = cu_hist[s + 1] - h_off;
   const int prob = s * Hkv + h;
-  Threshold t;
-  find_threshold_bin<256>(hist + (int64_t)prob * kScoreBins, L, min(kv_budget, L), rs, &t.bstar,
-                          &t.above, &t.need);
-
+  // the tile's scores are requested before the threshold search over the
+  // histogram, so the two latencies overlap
   const float* srow = scores + (int64_t)h * TL + h_off;
   uint64_t* crow = cand + (int64_t)h * TL + h_off;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -63,6 +61,9 @@ __global__ __launch_bounds__(256) void topb_filter_kernel(
     const int key = k0 + i * 256 + threadIdx.x;
     sc[i] = key < L ? srow[key] : 0.f;
   }
+  Threshold t;
+  find_threshold_bin<256>(hist + (int64_t)prob * kScoreBins, L, min(kv_budget, L), rs, &t.bstar,
+                          &t.above, &t.need);
   uint32_t gt = 0, nc = 0;
   uint64_t bal[PER];
 #pragma unroll
@@ -151,21 +152,25 @@ __global__ __launch_bounds__(256) void topb_write_kernel(
   const int L = cu_hist[s + 1] - h_off;
   const int prob = s * Hkv + h;
   const Threshold t = thr[prob];
+  // the tile's scores are requested before the count of the tiles before it
+  const float* srow = scores + (int64_t)h * TL + h_off;
+  constexpr int PER = kTopbKeys / 256;
+  const int k0 = lt * kTopbKeys + threadIdx.x * PER;
+  float scv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) scv[e] = k0 + e < L ? srow[k0 + e] : 0.f;
 
   uint32_t before = 0;
   for (int i = kt_off[s] + threadIdx.x; i < tile; i += 256)
     before += gtcount[(int64_t)h * NKT + i] + chcount[(int64_t)h * NKT + i];
   before = block_sum<256>(before, rs);
 
-  const float* srow = scores + (int64_t)h * TL + h_off;
-  constexpr int PER = kTopbKeys / 256;
-  const int k0 = lt * kTopbKeys + threadIdx.x * PER;
   uint32_t flags = 0, cnt = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int key = k0 + e;
     if (key < L) {
-      const float sc = srow[key];
+      const float sc = scv[e];
       const int bin = bin_of<kRaw>(sc);
       const bool sel = bin > t.bstar ||
                        (bin == t.bstar && radix_taken<true>(cand_key(sc, key), t.prefix, t.mask));
