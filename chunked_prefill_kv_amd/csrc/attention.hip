@@ -192,7 +192,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     bf16* __restrict__ out) {
   using TT = AttnTile<D, NW>;
   constexpr int KT = TT::KT, NDS = D / 16, NDB = D / 32;
-  constexpr int kAttnRows = TT::ROWS;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][TT::K_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][TT::V_ELEMS];
 
@@ -209,25 +208,42 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;
   const int rows = C * G;
-  const int ntile = (rows + kAttnRows - 1) / kAttnRows;
-  if (bx >= ntile) return;
-  // Longest rows (most keys) first. When every workgroup is resident at once
-  // (pair_order), the first and second halves of the order fill a CU's two
-  // slots, so the second half runs from light to heavy: each CU then pairs a
-  // heavy tile with a light one instead of two of similar weight.
-  const int half = (ntile + 1) / 2;
-  const int tile = (pair_order && bx >= half) ? bx - half : ntile - 1 - bx;
+  // Rows come in 128-row tiles of four waves; an eight-wave workgroup takes
+  // two of them. Longest rows (most keys) first, except that with pair_order
+  // an eight-wave workgroup takes the u-th tile from the end and the u-th
+  // from the start: the K/V tiles they share are loaded once, the light half
+  // stops computing when its rows run out of keys, and every workgroup gets
+  // the same amount of work.
+  constexpr int NH = NW / 4;  // 128-row tiles per workgroup
+  const int n128 = (rows + 127) / 128;
+  const int nunit = (n128 + NH - 1) / NH;
+  if (bx >= nunit) return;
+  int th[NH];  // each half's 128-row tile, -1 = none
+  if constexpr (NH == 1) {
+    th[0] = nunit - 1 - bx;
+  } else if (pair_order) {
+    th[0] = n128 - 1 - bx;
+    th[1] = bx < n128 - 1 - bx ? bx : -1;
+  } else {
+    const int u = nunit - 1 - bx;
+    th[0] = 2 * u;
+    th[1] = 2 * u + 1 < n128 ? 2 * u + 1 : -1;
+  }
   const int h_off = cu_hist[s];
   const int Lh = cu_hist[s + 1] - h_off;
   const int B_eff = min(kv_budget, Lh);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int col = lane & 31, hi = lane >> 5;
-  const int r = tile * kAttnRows + wave * 32 + col;
-  const bool rvalid = r < rows;
+  const int my_tile = th[wave / 4];
+  const int row0 = max(my_tile, 0) * 128 + (wave % 4) * 32;  // the wave's first row
+  const bool wave_live = my_tile >= 0 && row0 < rows;
+  const int r = row0 + col;
+  const bool rvalid = wave_live && r < rows;
   const int t = rvalid ? r / G : 0;
   const int jh = h * G + (rvalid ? r % G : 0);
-  const int t_wave_first = min(C - 1, (tile * kAttnRows + wave * 32) / G);
+  const int t_wave_first = min(C - 1, row0 / G);
+  const int t_wave_last = min(C - 1, (row0 + 31) / G);
 
   bf16x8 qreg[NDS];
   {
@@ -238,7 +254,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
       qreg[ds] = rvalid ? v : (bf16x8){};
     }
   }
-  const int t_last = min(C - 1, (tile * kAttnRows + kAttnRows - 1) / G);
+  int top = th[0];
+#pragma unroll
+  for (int i = 1; i < NH; ++i) top = max(top, th[i]);
+  const int t_last = min(C - 1, (top * 128 + 127) / G);  // the workgroup's last token
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = (f32x16){};
@@ -315,7 +334,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const int kbase = (ph1 ? it : it - n1) * KT;
     const bf16* ks = Ks[buf] + k_rd;
     const bf16* vs = Vs[buf] + v_rd;
-
+    // a wave without rows, or whose rows' tokens all precede this chunk
+    // tile, only helps with the loads
+    if (wave_live && (ph1 || kbase <= t_wave_last)) {
     __builtin_amdgcn_s_setprio(1);
     // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks, interleaved)
     f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
@@ -411,6 +432,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pb[sb][kk], oacc[db], 0, 0, 0);
       }
     __builtin_amdgcn_s_setprio(0);
+    }
     if (it + 1 < n_all) attn_store_tile<D, NW>(Ks[buf ^ 1], Vs[buf ^ 1], kr, vr);
     __syncthreads();
   }
@@ -447,20 +469,23 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
   const float sl2 = scale * kLog2e;
   if (p.dtype == QUOKA_BF16) {
     const int64_t rows = (int64_t)p.maxC * p.G;
+    const int64_t n128 = (rows + 127) / 128;
+    const int64_t grid4 = n128 * p.Hkv * p.S;  // four-wave workgroups the shape needs
+    // eight waves on 256 contiguous rows when that still leaves two workgroups
+    // per CU; eight waves on a heavy and a light 128-row tile when four-wave
+    // workgroups would fill the chip exactly once (then pairing balances the
+    // CUs and shares the K/V loads); else four waves
     const bool wide = (rows + 255) / 256 * p.Hkv * p.S >= kAttnWideMinBlocks;
-    const int nw = wide ? 8 : 4;
-    const int ntile = (int)((rows + nw * 32 - 1) / (nw * 32));
+    const int pair = (!wide && grid4 > 256 && grid4 <= kAttnResident4) ? 1 : 0;
+    const int nw = (wide || pair) ? 8 : 4;
+    const int ntile = (int)(nw == 8 ? (n128 + 1) / 2 : n128);
     dim3 grid((unsigned)(ntile * p.Hkv * p.S));
-    // pair heavy and light tiles when the whole grid is resident: an XCD's
-    // CUs take their first and second workgroups from the first and second
-    // halves of its share of the order
-    const int pair = (!wide && (int64_t)ntile * p.Hkv * p.S <= kAttnResident4) ? 1 : 0;
 #define QUOKA_ATTN(D, NW, IDX)                                                                 \
   hipLaunchKernelGGL((attn_mfma_kernel<D, NW, IDX>), grid, dim3(NW * 64), 0, st, (const bf16*)q, \
                      (const bf16*)k_sel, (const bf16*)v_sel, sel, (const bf16*)k_chunk,           \
                      (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,          \
                      p.kv_budget, ntile, pair, sl2, (bf16*)out)
-#define QUOKA_ATTN_NW(D, IDX) { if (wide) QUOKA_ATTN(D, 8, IDX); else QUOKA_ATTN(D, 4, IDX); }
+#define QUOKA_ATTN_NW(D, IDX) { if (nw == 8) QUOKA_ATTN(D, 8, IDX); else QUOKA_ATTN(D, 4, IDX); }
     if (sel) { if (p.D == 128) QUOKA_ATTN_NW(128, true) else QUOKA_ATTN_NW(64, true) }
     else     { if (p.D == 128) QUOKA_ATTN_NW(128, false) else QUOKA_ATTN_NW(64, false) }
 #undef QUOKA_ATTN_NW

@@ -1,7 +1,8 @@
 """GPU parity of every stage against the fp64 oracle, at sizes the oracle
 finishes in seconds (several tiles per kernel plus ragged tails), and the edge
 cases: empty history, one-token chunk, budgets above the data, the largest
-query budget, zero vectors, head_dim 64 and 128, GQA groups of 1, 2, 4 and 7.
+query budget, zero vectors, head_dim 64 and 128, GQA groups of 1, 2, 4, 7 and 8,
+and decode-like batches (every chunk one or two tokens).
 """
 import math
 
@@ -31,6 +32,10 @@ CASES = {
     "bf16_budget_above_data": ([(90, 50), (40, 500)], 8, 2, 128, "bf16", 200 // 2, 600, {}),
     "bf16_needles": ([(256, 3000), (128, 1500)], 8, 2, 128, "bf16", 8, 32,
                      dict(needles_per_head=4, outlier_needles=6.0)),
+    # decode-like chunks (C_s * G <= 8): the split-key attention kernel
+    "bf16_decode_g4": ([(1, 3000), (1, 0), (2, 500), (1, 64)], 8, 2, 128, "bf16", 1, 256, {}),
+    "bf16_decode_g8": ([(1, 1500), (1, 70)], 16, 2, 128, "bf16", 2, 1000, dict(scaled=True)),
+    "bf16_decode_d64_g1": ([(1, 2000), (1, 100), (1, 1)], 2, 2, 64, "bf16", 1, 300, {}),
 }
 
 
@@ -73,7 +78,7 @@ def test_fused_equals_stagewise():
 def test_fused_gather_handles_padding_and_bad_indices():
     """chunk_attn_gather == gather + chunk_attn when sel_idx holds -1 padding in the middle and
     indices outside [0, L_s) (both read as zero rows), for both kernels (bf16 MFMA, fp32)."""
-    for name in ("bf16_d128_g4_ragged", "fp32_d128_g2_ragged"):
+    for name in ("bf16_d128_g4_ragged", "fp32_d128_g2_ragged", "bf16_decode_g4"):
         print(f"[gpu] fused gather, bad indices {name}", flush=True)
         w = _case(name)
         shape, t = upload(w)
