@@ -134,6 +134,75 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_runs: int = 5):
     }
 
 
+def bench_peaks():
+    """Measured peaks next to the published ones the rooflines divide by: a loop of
+    independent v_mfma_f32_32x32x16_bf16 on every SIMD (two waves each), a streaming
+    16-byte read of 4 GiB, a 2 GiB device copy, and the shader cycle counter against the
+    100 MHz real-time counter."""
+    import ctypes
+    import torch
+    from chunked_prefill_kv_amd import build as cbuild
+    if not os.path.exists(cbuild.PEAKS_LIB):
+        raise RuntimeError(f"{cbuild.PEAKS_LIB} is missing: build it first")
+    lib = ctypes.CDLL(cbuild.PEAKS_LIB)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.quoka_peaks_mfma.argtypes = [i32, i32, vp, vp]
+    lib.quoka_peaks_read.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
+    lib.quoka_peaks_clock.argtypes = [i32, vp, vp, vp]
+    lib.quoka_peaks_device.argtypes = [ctypes.POINTER(i32)] * 4
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    st = torch.cuda.current_stream().cuda_stream
+    info = [ctypes.c_int(0) for _ in range(4)]
+    assert lib.quoka_peaks_device(*[ctypes.byref(x) for x in info]) == 0
+    clock_khz, mem_khz, bus_bits, cus = (x.value for x in info)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3  # seconds
+
+    blocks, iters = cus * 2, 20000  # two four-wave workgroups per CU: two waves per SIMD
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    t = timed(lambda: lib.quoka_peaks_mfma(blocks, iters, sink.data_ptr(), st), 3)
+    mfma_tflops = blocks * 4 * iters * 4 * 32768 / t / 1e12
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    rblocks = cus * 16
+    rsink = torch.empty(rblocks * 256, dtype=torch.float32, device=dev)
+    t = timed(lambda: lib.quoka_peaks_read(buf.data_ptr(), buf.numel(), rblocks,
+                                           rsink.data_ptr(), st), 5)
+    read_gbs = buf.numel() / t / 1e9
+    src = buf[: 2 << 30]
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 5)
+    copy_gbs = 2 * src.numel() / t / 1e9
+    del buf, dst
+    cnt = torch.zeros(4, dtype=torch.int64, device=dev)
+    csink = torch.empty(64, dtype=torch.float32, device=dev)
+    assert lib.quoka_peaks_clock(1 << 22, cnt.data_ptr(), csink.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    t0, t1, r0, r1 = (int(x) for x in cnt.cpu())
+    memtime_mhz = (t1 - t0) / ((r1 - r0) / 100e6) / 1e6 if r1 > r0 else None
+    # dense bf16: 1024 flop per clock per SIMD, four SIMDs per CU
+    mfma_clock_mhz = mfma_tflops * 1e12 / (cus * 4 * 1024) / 1e6
+    print(json.dumps({
+        "probe": "peaks", "cus": cus, "clock_rate_attr_MHz": clock_khz / 1e3,
+        "memory_clock_attr_MHz": mem_khz / 1e3, "memory_bus_bits": bus_bits,
+        "mfma_bf16_dense_TFLOPs": round(mfma_tflops, 1),
+        "mfma_frac_of_published_2500": round(mfma_tflops / PEAK_BF16_TFLOPS, 3),
+        "mfma_implied_clock_MHz": round(mfma_clock_mhz, 1),
+        "hbm_read_GBps": round(read_gbs, 1), "hbm_copy_GBps": round(copy_gbs, 1),
+        "hbm_read_frac_of_published_8000": round(read_gbs / PEAK_HBM_GBS, 3),
+        "shader_counter_MHz": None if memtime_mhz is None else round(memtime_mhz, 1),
+    }), flush=True)
+
+
 def bench_prompt(args):
     """Whole-prompt chunked prefill of one sequence (llama8b heads: 32/8, d=128, bf16,
     N_q=64, B=2048): quoka_prefill_prompt against dense chunked prefill, where every chunk
@@ -220,6 +289,9 @@ def main():
     ap.add_argument("--variant", default="quoka",
                     choices=["quoka", "dot", "mean_queries", "mean_query", "per_head", "global"],
                     help="time a baseline selection (quoka_select_variant) in place of QUOKA's")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only confirm the chip's peaks (dense bf16 MFMA loop, HBM streaming "
+                         "read and copy, shader clock) and print them as one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times) and exit: the "
                          "reference for scaling HBM byte counters")
@@ -241,6 +313,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
+
+    if args.peaks:
+        bench_peaks()
         return
 
     if args.prompt:

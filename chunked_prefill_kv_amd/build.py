@@ -1,4 +1,5 @@
-"""Build libquoka.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Build libquoka.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+libquoka_peaks.so (the bench's peak probes).
 
 Usage: python -m chunked_prefill_kv_amd.build   (or build() from Python)
 Objects go to _build/ at the repository root; the library lands in
@@ -19,6 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(ROOT, "_build", "quoka")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libquoka.so")
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(LIB_DIR, "libquoka_peaks.so")
 ARCH = "gfx950"
 
 
@@ -72,8 +75,12 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    # the peak probes the bench confirms the roofline denominators with
+    tmp = PEAKS_LIB + ".tmp"
+    _run([cc, *flags, "-shared", PEAKS_SRC, "-o", tmp])
+    os.replace(tmp, PEAKS_LIB)
     if verbose:
-        print(f"built {LIB_PATH}", flush=True)
+        print(f"built {LIB_PATH} and {PEAKS_LIB}", flush=True)
     return LIB_PATH
 
 

@@ -140,3 +140,15 @@ def test_select_variant_validation(lib, variant, cu_chunk, hq, qb, code, msg):
     st = lib.quoka_select_variant(ctypes.byref(shape.c), variant, p, p, qb, 8, p, None, None,
                                   None, None, 0, None)
     assert st == code and msg in lib.quoka_last_error().decode()
+
+
+def test_peak_probe_library_exports_its_probes(lib):
+    """The bench's peak probes are a library of their own, outside the boundary."""
+    path = cbuild.PEAKS_LIB
+    if not os.path.exists(path):
+        cbuild.build()
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    names = set(re.findall(r"\bT (quoka_peaks_\w+)", out))
+    assert names == {"quoka_peaks_mfma", "quoka_peaks_read", "quoka_peaks_clock",
+                     "quoka_peaks_device"}
