@@ -380,9 +380,14 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
-    sel_us = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    gat_us = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    att_us = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    per = {"select": np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3,
+           "gather": np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3,
+           "attention": np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3}
+    sel_us, gat_us, att_us = (float(np.mean(per[k])) for k in ("select", "gather", "attention"))
+    pct = {k: {"p10": round(float(np.percentile(v, 10)), 2),
+               "p50": round(float(np.percentile(v, 50)), 2),
+               "p90": round(float(np.percentile(v, 90)), 2)}
+           for k, v in per.items() if args.unfused or k != "gather"}
 
     tokens = float(w.cu_chunk[-1])
     flops = attention_flops(w)
@@ -412,6 +417,7 @@ def main():
                    "input_sets": len(sets), "selection": args.variant,
                    "path": "select + gather + chunk_attn" if args.unfused
                            else "select + chunk_attn_gather (gather fused)"},
+        "stages_us_pct": pct,
         "stages_us": ({"select": round(sel_us, 2), "gather": round(gat_us, 2),
                        "chunk_attn": round(att_us, 2)} if args.unfused else
                       {"select": round(sel_us, 2), "chunk_attn_gather": round(att_us, 2)}),
