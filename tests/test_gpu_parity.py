@@ -162,3 +162,30 @@ def test_binding_rejects_wrong_inputs():
         cpk.select(shape, t["q"], t["k_hist"], 8, 16,
                    workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
     assert e.value.status == cpk.QUOKA_EWORKSPACE
+
+
+ORDER_CASES = {
+    # eight-wave workgroups pairing a heavy and a light 128-row tile; 33 tiles
+    # leave the middle one without a partner
+    "pair_odd": ([(1056, 3000)], 32, 8, 128, "bf16", 16, 512),
+    # the paired order over a ragged batch: the shorter chunk needs fewer pairs
+    "pair_ragged": ([(1024, 2000), (500, 1500)], 32, 8, 128, "bf16", 16, 512),
+    # 256 contiguous rows per workgroup; the last workgroup has one tile only
+    "wide_odd": ([(1056, 600)] * 8, 32, 8, 128, "bf16", 8, 256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ORDER_CASES))
+def test_attention_tile_orders(name):
+    """The attention's workgroup orders (paired, wide, odd tile counts) against the oracle
+    on sampled rows, and the fused gather bit-identical to gather + attend."""
+    seqs, hq, hkv, d, dt, nq, b = ORDER_CASES[name]
+    print(f"[gpu] attention order {name}", flush=True)
+    w = make_case(seqs, hq, hkv, d, dt, nq, b, seed=31, name=name)
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    check_invariants(w, r)
+    check_selection(w, r)
+    err = check_attention(w, r, rows=48, rng=np.random.default_rng(5))
+    assert np.array_equal(r["out_fused"], r["out"])
+    print(f"[gpu] {name}: attention max-abs {err:.3g}", flush=True)
