@@ -346,8 +346,10 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
 // bf16 (kMfma): hi/lo bf16 pairs in MFMA A-operand order, 16-row blocks,
 // layout [block][head][d-step][term][lane] of bf16x8; rows past the last
 // repeat row 0 (which leaves a max unchanged). fp32: rows [row][head][d].
+constexpr int kQselThreads = 512;  // threads of the one workgroup per (sequence, KV head)
+
 template <int D, bool kMfma>
-__global__ __launch_bounds__(kQprepThreads) void qselect_kernel(
+__global__ __launch_bounds__(kQselThreads) void qselect_kernel(
     const void* __restrict__ qv, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int Hq, int Hkv,
     int G, int64_t TC, const float* __restrict__ g, const double* __restrict__ gpart,
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(kQprepThreads) void qselect_kernel(
     int32_t* __restrict__ qidx, void* __restrict__ gsel, int kv_budget,
     int32_t* __restrict__ sel_idx) {
   using T = typename std::conditional<kMfma, bf16, float>::type;
-  constexpr int NT = kQprepThreads;
+  constexpr int NT = kQselThreads;
   const T* q = (const T*)qv;
   const int prob = blockIdx.x, s = prob / Hkv, h = prob % Hkv;
   const int c_off = cu_chunk[s];
@@ -530,7 +532,8 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
   }
   const dim3 sgrid((unsigned)(p.S * p.Hkv));
 #define QUOKA_QSEL(D, M)                                                                      \
-  hipLaunchKernelGGL((qselect_kernel<D, M>), sgrid, block, 0, st, q, p.cu_chunk, p.cu_hist,   \
+  hipLaunchKernelGGL((qselect_kernel<D, M>), sgrid, dim3(kQselThreads), 0, st, q, p.cu_chunk,   \
+                     p.cu_hist,                                                               \
                      plan, p.Hq, p.Hkv, p.G, p.TC, g, gpart, qcos, p.q_budget, p.nq_pad,      \
                      p.variant, qidx, (void*)(ws + w.gsel), p.kv_budget, sel_idx)
   const bool mfma = p.dtype == QUOKA_BF16;
