@@ -209,7 +209,7 @@ quoka_status run_select(const Problem& p, const Workspace& w, const void* q, con
   float* qcos = qcos_opt ? qcos_opt : (float*)(ws + w.qcos);
   float* scores = scores_opt ? scores_opt : (float*)(ws + w.scores);
   int32_t* qidx = q_idx_opt ? q_idx_opt : (int32_t*)(ws + w.qidx);
-  if ((rc = hip_check(launch_qprep(p, q, ws, w, qcos, qidx, sel_idx, st), "qprep", st)))
+  if ((rc = hip_check(launch_qprep(p, q, ws, w, qcos, qcos_opt != nullptr, qidx, sel_idx, st), "qprep", st)))
     return rc;
   if ((rc = hip_check(launch_scorer(p, k_hist, ws, w, scores, st), "scorer", st))) return rc;
   return hip_check(launch_topb(p, ws, w, scores, sel_idx, st), "topb", st);

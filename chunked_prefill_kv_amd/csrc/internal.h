@@ -92,8 +92,11 @@ hipError_t set_scorer_lds_limit(int bytes, int bytes_heads);
 
 // Plan and counter clearing, query prep, cosines and the lowest-cosine
 // select; also writes the -1 padding of sel_idx past each problem's B_eff.
+// want_cos: the caller asked for the cosines (else they are computed only when
+// some chunk has more tokens than q_budget, i.e. when the subselection needs them).
 hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
-                        float* qcos, int32_t* qidx, int32_t* sel_idx, hipStream_t st);
+                        float* qcos, bool want_cos, int32_t* qidx, int32_t* sel_idx,
+                        hipStream_t st);
 size_t scorer_lds_bytes(const Problem& p);
 hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const Workspace& w,
                          float* scores, hipStream_t st);

@@ -494,7 +494,8 @@ __global__ __launch_bounds__(kQselThreads) void qselect_kernel(
 }
 
 hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspace& w,
-                        float* qcos, int32_t* qidx, int32_t* sel_idx, hipStream_t st) {
+                        float* qcos, bool want_cos, int32_t* qidx, int32_t* sel_idx,
+                        hipStream_t st) {
   int32_t* plan = (int32_t*)(ws + w.plan);
   float* g = (float*)(ws + w.g);
   double* gpart = (double*)(ws + w.gpart);
@@ -519,8 +520,11 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
 #undef QUOKA_QPREP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.variant == QUOKA_VARIANT_MEAN_QUERY) {
-      // no subselection: the cosines are not needed
+    // the select keeps every token of a chunk that has at most q_budget of them,
+    // whatever their cosines; the mean-query baseline does not subselect at all
+    const bool need_cos =
+        p.variant != QUOKA_VARIANT_MEAN_QUERY && (want_cos || p.maxC > p.q_budget);
+    if (!need_cos) {
     } else if (p.D == 128)
       hipLaunchKernelGGL((qprep_cos_kernel<128>), grid, block, 0, st, p.cu_chunk, plan, p.S,
                          p.Hkv, p.TC, g, gpart, qcos);

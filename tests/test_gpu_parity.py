@@ -189,3 +189,16 @@ def test_attention_tile_orders(name):
     err = check_attention(w, r, rows=48, rng=np.random.default_rng(5))
     assert np.array_equal(r["out_fused"], r["out"])
     print(f"[gpu] {name}: attention max-abs {err:.3g}", flush=True)
+
+
+def test_cosines_skipped_when_every_token_is_kept():
+    """With every chunk at most q_budget tokens long the cosine pass is skipped unless the
+    caller asks for the cosines; the selections are the same either way."""
+    w = _case("bf16_decode_g4")
+    shape, t = upload(w)
+    a = cpk.select(shape, t["q"], t["k_hist"], 4, w.budget, want_q_idx=True, want_scores=True)
+    b = cpk.select(shape, t["q"], t["k_hist"], 4, w.budget, want_q_idx=True, want_qcos=True,
+                   want_scores=True)
+    torch.cuda.synchronize()
+    for k in ("sel_idx", "q_idx", "scores"):
+        assert torch.equal(a[k], b[k]), k
