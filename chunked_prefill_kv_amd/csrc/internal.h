@@ -14,7 +14,7 @@ namespace quoka {
 constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
 constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup...
 constexpr int kScoreKeysSmall = 512; // ...or half as many when that fills the CUs better
-constexpr int kScoreMinBlocks = 512; // scorer workgroups wanted (two per CU)
+constexpr int kScoreMinBlocks = 1024; // scorer workgroups wanted (four per CU)
 constexpr int kTopbKeys = 2048;      // history keys per top-B workgroup
 constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
 constexpr int kQselCap = 12288;      // chunk tokens whose cosines the query select stages in LDS
