@@ -337,7 +337,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     // a wave without rows, or whose rows' tokens all precede this chunk
     // tile, only helps with the loads
     if (wave_live && (ph1 || kbase <= t_wave_last)) {
-    __builtin_amdgcn_s_setprio(1);
     // S^T = K Q^T for the 64 keys of the tile (two 32-key blocks, interleaved)
     f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
     // all 16 K operands are read before the MFMAs so LDS latency overlaps
@@ -355,7 +354,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
-    __builtin_amdgcn_s_setprio(0);
     // masks: history tail past B_eff; causal on tiles reaching past the
     // wave's first token
     const bool need_mask = ph1 ? (kbase + KT > B_eff) : (kbase + KT - 1 > t_wave_first);
@@ -412,7 +410,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
         l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, l_part, false);
         l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, l_part, false);
       }
-    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T; the A operand is read transposed from row-major V: lane
     // group g = lane/16 covers d0 = db*32 + (g&1)*16, keys kb0 = ... + hi*4
 #pragma unroll
@@ -431,7 +428,6 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
         for (int db = 0; db < NDB; ++db)
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pb[sb][kk], oacc[db], 0, 0, 0);
       }
-    __builtin_amdgcn_s_setprio(0);
     }
     if (it + 1 < n_all) attn_store_tile<D, NW>(Ks[buf ^ 1], Vs[buf ^ 1], kr, vr);
     __syncthreads();
