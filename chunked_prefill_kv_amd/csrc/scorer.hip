@@ -76,25 +76,40 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
       for (int ds = 0; ds < NDS; ++ds)
         b[kb][ds] = buffer_load_bf16x8(rk, (k0 + kb * 16) * row_bytes + lane_off + ds * 64u);
   };
-  // the first key block is requested before the kept queries are staged
-  bf16x8 b0[4][NDS], b1[4][NDS];
-  if (k_begin + wave * 64 < k_end) load(0, b0);
-
+  // The kept-query rows are read (into registers) and stored to LDS before
+  // any key is requested: requested after the keys, their reads wait behind
+  // the whole key stream of the chip. Then the first two key blocks of every
+  // wave go out together, so the stream has no gap between the rounds.
   extern __shared__ char smem[];
   uint32_t* lhist = (uint32_t*)smem;                       // kScoreBins
   bf16x8* lg = (bf16x8*)(smem + kScoreBins * 4);           // nqb * NDS * 2 * 64
+  const bf16x8* gsrc = gsel + (int64_t)prob * (nq_pad / 16) * GH * NDS * 2 * 64;
+  const int nstage = nqb * GH * NDS * 2 * 64;
+  constexpr int kStageU = 8;  // 16-byte pieces per thread staged through registers
+  bf16x8 stg[kStageU];
+#pragma unroll
+  for (int u = 0; u < kStageU; ++u) {
+    const int i = u * 256 + (int)threadIdx.x;
+    if (i < nstage) stg[u] = gsrc[i];
+  }
+  bf16x8 b0[4][NDS], b1[4][NDS];
   for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
-  block_copy<256, 8>(lg, gsel + (int64_t)prob * (nq_pad / 16) * GH * NDS * 2 * 64,
-                     nqb * GH * NDS * 2 * 64);
+#pragma unroll
+  for (int u = 0; u < kStageU; ++u) {
+    const int i = u * 256 + (int)threadIdx.x;
+    if (i < nstage) lg[i] = stg[u];
+  }
+  if (k_begin + wave * 64 < k_end) load(0, b0);
+  if (NIT > 1 && k_begin + 256 + wave * 64 < k_end) load(1, b1);
+  if (nstage > kStageU * 256)
+    block_copy<256, 8>(lg + kStageU * 256, gsrc + kStageU * 256, nstage - kStageU * 256);
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     bf16x8 (&cur)[4][NDS] = (it & 1) ? b1 : b0;
-    bf16x8 (&nxt)[4][NDS] = (it & 1) ? b0 : b1;
     const int k0 = k_begin + it * 256 + wave * 64;
-    if (it + 1 < NIT && k0 + 256 < k_end) load(it + 1, nxt);
     if (k0 >= k_end) break;
     float nsq[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
@@ -152,6 +167,8 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
       srow[key] = sc;
       atomicAdd(&lhist[MODE == kModeDot ? score_bin_raw(sc) : score_bin(sc)], 1u);
     }
+    // the block just scored is refilled with the one two rounds ahead
+    if (it + 2 < NIT && k0 + 512 < k_end) load(it + 2, cur);
   }
   __syncthreads();
   flush_hist(lhist, hist, prob);
