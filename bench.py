@@ -10,9 +10,11 @@ the CPU baseline). Several rotated copies of the inputs are
 cycled through so that consecutive steps do not hit the 256 MB last-level
 cache with the previous step's history keys.
 
-Prints ONE JSON line. The roofline entry is for the dominant kernel (chunk
-attention, bf16 MFMA); its duration is measured live with HIP events around
-that single launch on the stream it runs on. cpu_baseline times the fp64
+Prints ONE JSON line. `value` comes from a timed pass of the steps alone; a
+second timed pass brackets every stage with HIP events on the stream the
+kernels run on (they cost the stream ~10 us per step, so they are kept out of
+the first pass) and gives the stage times and the roofline entry for the
+dominant kernel (chunk attention, bf16 MFMA). cpu_baseline times the fp64
 oracle on a bounded sample of the same workload on the host cores.
 
 usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config llama8b]
@@ -370,16 +372,25 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Two timed passes of `steps` steps each. The first times the steps alone:
+    # `value` and ms_per_step. The second brackets every stage with events on
+    # the stream the kernels run on, for the stage times and the roofline's
+    # kernel duration; those events themselves cost the stream ~10 us per step,
+    # so the step time is not taken from that pass.
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
     per = {"select": np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3,
            "gather": np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3,
            "attention": np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3}
