@@ -12,8 +12,6 @@
 #include "common.h"
 #include "internal.h"
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 namespace quoka {
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -114,14 +114,17 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     float nsq[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int kb = 0; kb < 4 && MODE != kModeDot; ++kb) {
+      // |k|^2 from bf16 pairs: two exact products per instruction, fp32 sums
       float ss = 0.f;
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds)
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 v = cur[kb][ds];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (float)cur[kb][ds][e];
-          ss = fmaf(x, x, ss);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {v[e], v[e + 1]};
+          ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
         }
+      }
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
       nsq[kb] = ss;
