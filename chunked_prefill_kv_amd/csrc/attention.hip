@@ -12,6 +12,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace quoka {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -115,8 +117,9 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 // K/V tiles of 64 keys: first the kept history (masked past B_eff), then the
 // chunk's keys up to the workgroup's last token (causal mask per row, only
 // on tiles that reach past a wave's first token). LDS is double buffered:
-// while a tile is consumed, the next one is in flight from HBM/L2 into VGPRs
-// and lands in the other buffer; one barrier per tile.
+// while a tile is consumed, the next one is in flight from HBM/L2 straight
+// into the other buffer (buffer loads that write LDS, no register staging;
+// an out-of-range load writes zeros); one barrier per tile.
 // Blocks are renumbered so that all tiles of one KV head run on one XCD
 // (blocks are dealt round-robin to the 8 XCDs) and share its L2.
 // ---------------------------------------------------------------------------
@@ -127,47 +130,7 @@ struct AttnTile {
   static constexpr int KT = 64;                  // keys per tile
   static constexpr int NT = NW * 64;             // threads
   static constexpr int ROWS = NW * 32;           // query rows per workgroup
-  static constexpr int KSTR = D + 8;             // K row stride in LDS (elements)
-  static constexpr int VSTR = D + 32;            // V row stride in LDS (elements)
-  static constexpr int NCH = KT * D / 8 / NT;    // 16-byte chunks per thread, K and V each
-  static constexpr int K_ELEMS = KT * KSTR;
-  static constexpr int V_ELEMS = KT * VSTR;
 };
-
-// Global -> registers: thread takes 16-byte chunks c = tid + NT i of the
-// 64 x D tile (row c / (D/8)). The buffer resources start at the tile's first
-// row and end at the last valid row, so rows past the end read as zeros
-// without any per-element select.
-template <int D, int NW>
-__device__ __forceinline__ void attn_load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                               uint32_t row_bytes,
-                                               bf16x8 (&kr)[AttnTile<D, NW>::NCH],
-                                               bf16x8 (&vr)[AttnTile<D, NW>::NCH]) {
-  using TT = AttnTile<D, NW>;
-#pragma unroll
-  for (int i = 0; i < TT::NCH; ++i) {
-    const int c = threadIdx.x + TT::NT * i;
-    const uint32_t off = (uint32_t)(c / (D / 8)) * row_bytes + (uint32_t)(c % (D / 8)) * 16u;
-    kr[i] = buffer_load_bf16x8(rk, off);
-    vr[i] = buffer_load_bf16x8(rv, off);
-  }
-}
-
-// Registers -> LDS, both row-major (key, d). V is transposed later by the
-// LDS transpose read that feeds the P.V MFMA.
-template <int D, int NW>
-__device__ __forceinline__ void attn_store_tile(bf16* __restrict__ Ks, bf16* __restrict__ Vs,
-                                                const bf16x8 (&kr)[AttnTile<D, NW>::NCH],
-                                                const bf16x8 (&vr)[AttnTile<D, NW>::NCH]) {
-  using TT = AttnTile<D, NW>;
-#pragma unroll
-  for (int i = 0; i < TT::NCH; ++i) {
-    const int c = threadIdx.x + TT::NT * i;
-    const int row = c / (D / 8), part = c % (D / 8);
-    *(bf16x8*)&Ks[row * TT::KSTR + part * 8] = kr[i];
-    *(bf16x8*)&Vs[row * TT::VSTR + part * 8] = vr[i];
-  }
-}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -190,8 +153,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     bf16* __restrict__ out) {
   using TT = AttnTile<D, NW>;
   constexpr int KT = TT::KT, NDS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][TT::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][TT::V_ELEMS];
+  // K and V tiles land straight from global memory (buffer loads into LDS),
+  // two buffers each, unpadded 2D-byte rows with XOR-swizzled 16-byte chunks
+  __shared__ __attribute__((aligned(1024))) bf16 Ks0[KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks1[KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs0[KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs1[KT * D];
 
   // XCD-aware renumbering: linear block L runs on XCD L % 8; give XCD x a
   // contiguous range of logical ids (tile-fastest, then head, then sequence).
@@ -277,19 +244,35 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   const uint32_t end2 = (uint32_t)t_last * rb2 + D * 2u;
   const int32_t* sidx = sel + prob * kv_budget;
 
-  bf16x8 kr[TT::NCH], vr[TT::NCH];
+  // Direct loads: a wave instruction writes 1 KB of LDS (lane l at +16 l),
+  // i.e. RPP rows of CPR 16-byte chunks; lane l of piece P takes row
+  // P*RPP + l/CPR and fetches the chunk that belongs in slot l%CPR: chunk
+  // slot ^ (row & 7) for K, slot ^ 2(row & 3) for V (the swizzles that keep
+  // the K row reads and the V transpose reads free of bank conflicts).
+  constexpr int CPR = D / 8, RPP = 64 / CPR, NP = KT / RPP / NW;  // pieces per wave per tensor
+  static_assert(NP >= 1 && KT % (RPP * NW) == 0, "tile must split into whole pieces per wave");
+  int prow[NP];
+  uint32_t kcol[NP], vcol[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int r = (wave * NP + u) * RPP + lane / CPR, sl = lane % CPR;
+    prow[u] = r;
+    kcol[u] = (uint32_t)(sl ^ (r & 7)) * 16u;
+    vcol[u] = (uint32_t)(sl ^ (2 * (r & 3))) * 16u;
+  }
   // kIdx: history row indices of the next tile to load, fetched one tile
   // ahead so that a row load never waits for its own index load
-  int nidx[TT::NCH];
-  auto fetch_idx = [&](int it) {
+  int nidx[NP];
+  auto fetch_idx = [&](int it) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TT::NCH; ++i) {
-      const int key = it * KT + (int)(threadIdx.x + TT::NT * i) / (D / 8);
-      nidx[i] = key < B_eff ? sidx[key] : -1;
+    for (int u = 0; u < NP; ++u) {
+      const int key = it * KT + prow[u];
+      nidx[u] = key < B_eff ? sidx[key] : -1;
     }
   };
   if (kIdx && n1 > 0) fetch_idx(0);
-  auto load = [&](int it) {
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  auto load = [&](int it, bf16* kd, bf16* vd) __attribute__((always_inline)) {
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
     if (kIdx && ph1) {
@@ -297,13 +280,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
       // out-of-range indices read at the end of the buffer, i.e. as zeros
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(k1, end1), rv = make_rsrc(v1, end1);
 #pragma unroll
-      for (int i = 0; i < TT::NCH; ++i) {
-        const int c = threadIdx.x + TT::NT * i;
-        const int row = nidx[i];
-        const uint32_t off = (unsigned)row < (unsigned)Lh
-                                 ? (uint32_t)row * rb1 + (uint32_t)(c % (D / 8)) * 16u : end1;
-        kr[i] = buffer_load_bf16x8(rk, off);
-        vr[i] = buffer_load_bf16x8(rv, off);
+      for (int u = 0; u < NP; ++u) {
+        const int row = nidx[u];
+        const bool ok = (unsigned)row < (unsigned)Lh;
+        const uint32_t base = (uint32_t)row * rb1;
+        bf16* kp = kd + (wave * NP + u) * 512;
+        bf16* vp = vd + (wave * NP + u) * 512;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(ok ? base + kcol[u] : end1), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(ok ? base + vcol[u] : end1), 0, 0, 0);
       }
       if (it + 1 < n1) fetch_idx(it + 1);
       return;
@@ -311,27 +295,48 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const uint32_t rb = ph1 ? rb1 : rb2;
     const uint32_t skip = (uint32_t)kbase * rb;
     const uint32_t left = (ph1 ? end1 : end2) - skip;
-    const bf16* kp = (ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2);
-    const bf16* vp = (ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2);
-    attn_load_tile<D, NW>(make_rsrc(kp, left), make_rsrc(vp, left), rb, kr, vr);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2), left);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2), left);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const uint32_t base = (uint32_t)prow[u] * rb;
+      bf16* kp = kd + (wave * NP + u) * 512;
+      bf16* vp = vd + (wave * NP + u) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(base + kcol[u]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(base + vcol[u]), 0, 0, 0);
+    }
   };
-  load(0);
-  attn_store_tile<D, NW>(Ks[0], Vs[0], kr, vr);
+  load(0, Ks0, Vs0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // lane-constant parts of the LDS read addresses
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int k_rd = col * TT::KSTR + hi * 8;                                  // K rows for S^T
-  const int v_rd = (hi * 4 + (j16 >> 2)) * TT::VSTR + (g16 & 1) * 16 + 4 * (j16 & 3);
+  // K operand of d-step ds: row sb*32 + col, chunk 2 ds + hi stored at
+  // chunk (2 ds + hi) ^ (col & 7); ds and ds + 4 differ by 8 chunks
+  int koff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) koff[j] = col * D + (((2 * j) ^ (hi ^ (col & 7))) << 3);
+  // V transpose reads: row hi*4 + j16/4 (+ tile offsets, all multiples of 4),
+  // columns db*32 + (g16&1)*16 + 4(j16&3); chunk c sits at c ^ 2(j16/4)
+  int voff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int c = db * 4 + (g16 & 1) * 2 + ((j16 & 3) >> 1);
+    voff[db] = (hi * 4 + (j16 >> 2)) * D + ((c ^ (2 * (j16 >> 2))) << 3) + 4 * (j16 & 1);
+  }
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
-  for (int it = 0; it < n_all; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_all) load(it + 1);
+  auto step = [&, B_eff, t_wave_first, t_wave_last, n1, n_all, t](int it, auto Bc)
+                  __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
+    bf16* kcur = B ? Ks1 : Ks0;
+    bf16* vcur = B ? Vs1 : Vs0;
+    if (it + 1 < n_all) load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
-    const bf16* ks = Ks[buf] + k_rd;
-    const bf16* vs = Vs[buf] + v_rd;
+    const bf16* ks = kcur;
+    const bf16* vs = vcur;
     // a wave without rows, or whose rows' tokens all precede this chunk
     // tile, only helps with the loads
     if (wave_live && (ph1 || kbase <= t_wave_last)) {
@@ -342,7 +347,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) ka[sb][ds] = *(const bf16x8*)(ks + sb * 32 * TT::KSTR + ds * 16);
+      for (int ds = 0; ds < NDS; ++ds)
+        ka[sb][ds] = *(const bf16x8*)(ks + sb * 32 * D + koff[ds & 3] + (ds >> 2) * 64);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
@@ -417,9 +423,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
         bf16x8 a[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16* p0 = vs + (sb * 32 + kk * 16) * TT::VSTR + db * 32;
+          const bf16* p0 = vs + (sb * 32 + kk * 16) * D + voff[db];
           const bf16x4 lo4 = lds_read_tr16(p0);
-          const bf16x4 hi4 = lds_read_tr16(p0 + 8 * TT::VSTR);
+          const bf16x4 hi4 = lds_read_tr16(p0 + 8 * D);
           a[db] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
@@ -427,8 +433,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], pb[sb][kk], oacc[db], 0, 0, 0);
       }
     }
-    if (it + 1 < n_all) attn_store_tile<D, NW>(Ks[buf ^ 1], Vs[buf ^ 1], kr, vr);
+    // this wave's loads of the next tile have landed; after the barrier
+    // every wave's have
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int it = 0; it < n_all; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_all) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   const float l_run = l_part + __shfl_xor(l_part, 32, 64);
