@@ -29,22 +29,108 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
 
+// ---- lane exchanges and wave reductions -------------------------------------
+// Exchanges stay in registers: DPP moves inside each 16-lane row, then
+// v_permlane16_swap / v_permlane32_swap across rows (a __shfl_xor would be an
+// LDS round trip per step). In every reduction each step combines a lane's
+// value with its partner's, so all lanes end with the same bits.
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1,0,3,2): lane ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1): lane ^ 2
+constexpr int kDppHalfMirror = 0x141; // lane 7 - i within each 8 (pairs the two quads)
+constexpr int kDppMirror = 0x140;     // lane 15 - i within each 16 (pairs the two halves)
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
+}
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<kCtrl>((uint32_t)v), hi = dpp_u32<kCtrl>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  return __longlong_as_double((long long)dpp_u64<kCtrl>((uint64_t)__double_as_longlong(v)));
+}
+// The lane's value and its partner's (lane ^ 16, resp. lane ^ 32), as a pair
+// whose order is the same in both lanes.
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// Sum / max over each 16-lane row (lanes 16r .. 16r + 15).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t row16_sum(uint32_t v) {
+  v += dpp_u32<kDppXor1>(v);
+  v += dpp_u32<kDppXor2>(v);
+  v += dpp_u32<kDppHalfMirror>(v);
+  v += dpp_u32<kDppMirror>(v);
+  return v;
+}
+// Sum / max of the four lanes l, l ^ 16, l ^ 32, l ^ 48.
+__device__ __forceinline__ float rows_sum(float v) {
+  uint32_t a, b;
+  swap16(__float_as_uint(v), a, b);
+  v = __uint_as_float(a) + __uint_as_float(b);
+  swap32(__float_as_uint(v), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  uint32_t a, b;
+  swap16(__float_as_uint(v), a, b);
+  v = fmaxf(__uint_as_float(a), __uint_as_float(b));
+  swap32(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ double rows_sum(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint32_t a0, b0, a1, b1;
+  swap16((uint32_t)u, a0, b0);
+  swap16((uint32_t)(u >> 32), a1, b1);
+  v = __longlong_as_double((long long)(((uint64_t)a1 << 32) | a0)) +
+      __longlong_as_double((long long)(((uint64_t)b1 << 32) | b0));
+  const uint64_t w = (uint64_t)__double_as_longlong(v);
+  swap32((uint32_t)w, a0, b0);
+  swap32((uint32_t)(w >> 32), a1, b1);
+  return __longlong_as_double((long long)(((uint64_t)a1 << 32) | a0)) +
+         __longlong_as_double((long long)(((uint64_t)b1 << 32) | b0));
+}
+__device__ __forceinline__ uint32_t rows_sum(uint32_t v) {
+  uint32_t a, b;
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
+}
+
 // ---- wave reductions (64 lanes, result in every lane) --------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return rows_sum(row16_sum(v)); }
+__device__ __forceinline__ double wave_sum(double v) { return rows_sum(row16_sum(v)); }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return rows_sum(row16_sum(v)); }
 
 // ---- order-preserving keys -------------------------------------------------
 // Monotone map float -> uint32: a < b (as floats) <=> key(a) < key(b); -0 and

@@ -152,8 +152,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) ss = fmaf(x[i][e], x[i][e], ss);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+      ss = row16_sum(ss);
       const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[i][e] = fmaf(x[i][e], inv, acc[i][e]);
@@ -168,8 +167,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       float v = acc[i][e];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
+      v = rows_sum(v);
       acc[i][e] = v / (float)G;
     }
     if (grp == 0 && t < C) {

@@ -43,8 +43,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, RadixScratc
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, RadixScratch<NT>& rs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum(v);
   if (lane == 0) rs.wsum[w] = v;
   __syncthreads();
   uint32_t t = 0;
@@ -62,6 +61,23 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, RadixScratch<NT>& rs) 
 // from the top, histogramming the keys that still match, until the bucket at
 // the boundary is taken whole (or every digit is fixed, when prefix is the
 // k-th key itself).
+// Bitwise and / or of a and o over the wave (result in every lane).
+__device__ __forceinline__ void wave_and_or(uint64_t& a, uint64_t& o) {
+  a &= dpp_u64<kDppXor1>(a); o |= dpp_u64<kDppXor1>(o);
+  a &= dpp_u64<kDppXor2>(a); o |= dpp_u64<kDppXor2>(o);
+  a &= dpp_u64<kDppHalfMirror>(a); o |= dpp_u64<kDppHalfMirror>(o);
+  a &= dpp_u64<kDppMirror>(a); o |= dpp_u64<kDppMirror>(o);
+  uint32_t x0, y0, x1, y1;
+  swap16((uint32_t)a, x0, y0); swap16((uint32_t)(a >> 32), x1, y1);
+  a = (((uint64_t)x1 << 32) | x0) & (((uint64_t)y1 << 32) | y0);
+  swap32((uint32_t)a, x0, y0); swap32((uint32_t)(a >> 32), x1, y1);
+  a = (((uint64_t)x1 << 32) | x0) & (((uint64_t)y1 << 32) | y0);
+  swap16((uint32_t)o, x0, y0); swap16((uint32_t)(o >> 32), x1, y1);
+  o = (((uint64_t)x1 << 32) | x0) | (((uint64_t)y1 << 32) | y0);
+  swap32((uint32_t)o, x0, y0); swap32((uint32_t)(o >> 32), x1, y1);
+  o = (((uint64_t)x1 << 32) | x0) | (((uint64_t)y1 << 32) | y0);
+}
+
 template <bool kLargest, int NT, typename KeyFn>
 __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch<NT>& rs, uint64_t& prefix,
                              uint64_t& mask) {
@@ -72,11 +88,7 @@ __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch<NT>& rs, u
     a &= key;
     o |= key;
   }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
-    a &= __shfl_xor(a, s, 64);
-    o |= __shfl_xor(o, s, 64);
-  }
+  wave_and_or(a, o);
   if (lane == 0) { rs.wand[w] = a; rs.wor[w] = o; }
   __syncthreads();
   a = ~0ull;

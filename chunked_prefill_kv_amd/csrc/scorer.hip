@@ -125,8 +125,7 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
           ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
         }
       }
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
+      ss = rows_sum(ss);
       nsq[kb] = ss;
     }
     float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -154,8 +153,7 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      m[kb] = fmaxf(m[kb], __shfl_xor(m[kb], 16, 64));
-      m[kb] = fmaxf(m[kb], __shfl_xor(m[kb], 32, 64));
+      m[kb] = rows_max(m[kb]);
     }
     // lane l stores key k0 + l: its column is l%16 of key block l/16
     const int kb = lane >> 4;
