@@ -443,7 +443,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     if (it + 1 < n_all) step(it + 1, std::integral_constant<int, 1>{});
   }
 
-  const float l_run = l_part + __shfl_xor(l_part, 32, 64);
+  uint32_t la, lb;
+  swap32(__float_as_uint(l_part), la, lb);  // the two lane halves of each query column
+  const float l_run = __uint_as_float(la) + __uint_as_float(lb);
   if (rvalid) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     bf16* orow = out + ((int64_t)(c_off + t) * Hq + jh) * D;

@@ -127,6 +127,23 @@ __device__ __forceinline__ uint32_t rows_sum(uint32_t v) {
   return a + b;
 }
 
+// Inclusive prefix sum over the 64 lanes: shifted adds inside each row
+// (row_shr 1, 2, 4, 8, lanes shifted in from outside the row add zero), then
+// lane 15 of each row into the next row and lane 31 into rows 2 and 3.
+template <int kCtrl, int kRowMask, bool kBoundZero>
+__device__ __forceinline__ uint32_t dpp_upd_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, kBoundZero);
+}
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += dpp_upd_u32<0x111, 0xF, true>(x);   // row_shr:1
+  x += dpp_upd_u32<0x112, 0xF, true>(x);   // row_shr:2
+  x += dpp_upd_u32<0x114, 0xF, true>(x);   // row_shr:4
+  x += dpp_upd_u32<0x118, 0xF, true>(x);   // row_shr:8
+  x += dpp_upd_u32<0x142, 0xA, false>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_upd_u32<0x143, 0xC, false>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // ---- wave reductions (64 lanes, result in every lane) --------------------
 __device__ __forceinline__ float wave_sum(float v) { return rows_sum(row16_sum(v)); }
 __device__ __forceinline__ double wave_sum(double v) { return rows_sum(row16_sum(v)); }

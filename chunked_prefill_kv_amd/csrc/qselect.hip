@@ -107,21 +107,16 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
   for (int s0 = 0, acc = 0; s0 < S; s0 += 64) {
     const int sq = s0 + lane;
     const int n = sq < S ? (cu_chunk[sq + 1] - cu_chunk[sq] + kQprepTokens - 1) / kQprepTokens : 0;
-    int incl = n;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
+    const int incl = (int)wave_inclusive_scan((uint32_t)n);
     const int excl = incl - n;
     const uint64_t m = __ballot(n > 0 && acc + excl <= tile && tile < acc + incl);
     if (m) {
       const int l = __ffsll((unsigned long long)m) - 1;
       s = s0 + l;
-      t_base = acc + __shfl(excl, l, 64);
+      t_base = acc + __builtin_amdgcn_readlane(excl, l);
       break;
     }
-    acc += __shfl(incl, 63, 64);
+    acc += __builtin_amdgcn_readlane(incl, 63);
   }
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;

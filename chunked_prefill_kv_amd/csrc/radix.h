@@ -21,12 +21,7 @@ struct RadixScratch {
 template <int NT>
 __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, RadixScratch<NT>& rs) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) rs.wsum[w] = x;
   __syncthreads();
   uint32_t add = 0;
