@@ -125,12 +125,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
 
-template <int D, int NW>
-struct AttnTile {
-  static constexpr int KT = 64;                  // keys per tile
-  static constexpr int NT = NW * 64;             // threads
-  static constexpr int ROWS = NW * 32;           // query rows per workgroup
-};
+constexpr int kAttnKeys = 64;  // keys per K/V tile
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -151,8 +146,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int S, int Hq,
     int Hkv, int G, int kv_budget, int ntile_max, int pair_order, float scale_log2,
     bf16* __restrict__ out) {
-  using TT = AttnTile<D, NW>;
-  constexpr int KT = TT::KT, NDS = D / 16, NDB = D / 32;
+  constexpr int KT = kAttnKeys, NDS = D / 16, NDB = D / 32;
   // K and V tiles land straight from global memory (buffer loads into LDS),
   // two buffers each, unpadded 2D-byte rows with XOR-swizzled 16-byte chunks
   __shared__ __attribute__((aligned(1024))) bf16 Ks0[KT * D];
