@@ -9,7 +9,7 @@ namespace quoka {
 template <int NT>
 struct RadixScratch {
   static constexpr int W = NT / 64;
-  uint32_t hist[256];
+  alignas(16) uint32_t hist[2][256];  // digit histograms, alternating between passes
   uint32_t wsum[W];
   uint64_t wand[W], wor[W];
   uint32_t digit;
@@ -102,25 +102,39 @@ __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch<NT>& rs, u
   mask = shift0 + 8 >= 64 ? 0ull : (~0ull << (shift0 + 8));
   prefix = a & mask;
   uint32_t rem = (uint32_t)k;
-  for (int shift = shift0; shift >= 0; shift -= 8) {
-    if (threadIdx.x < 256) rs.hist[threadIdx.x] = 0u;
-    __syncthreads();
+  // Each digit pass: one histogram of the keys still matching, then a single
+  // wave scans its 256 bins (4 per lane) and picks the digit. The two
+  // histograms alternate, so the one for the next pass is cleared by that
+  // wave meanwhile: two barriers per pass.
+  for (int i = threadIdx.x; i < 512; i += NT) (&rs.hist[0][0])[i] = 0u;
+  __syncthreads();
+  int hb = 0;
+  for (int shift = shift0; shift >= 0; shift -= 8, hb ^= 1) {
+    uint32_t* hist = rs.hist[hb];
     for (int i = threadIdx.x; i < N; i += NT) {
       const uint64_t key = key_of(i);
       if ((key & mask) == prefix) {
         uint32_t d = (uint32_t)(key >> shift) & 255u;
         if (kLargest) d = 255u - d;
-        atomicAdd(&rs.hist[d], 1u);
+        atomicAdd(&hist[d], 1u);
       }
     }
     __syncthreads();
-    const uint32_t v = threadIdx.x < 256 ? rs.hist[threadIdx.x] : 0u;
-    const uint32_t incl = block_inclusive_scan<NT>(v, rs);
-    const uint32_t excl = incl - v;
-    if (v > 0 && excl < rem && rem <= incl) {
-      rs.digit = threadIdx.x;
-      rs.rem = rem - excl;
-      rs.done = incl == rem;
+    if (w == 0) {
+      const uint4 c4 = ((const uint4*)hist)[lane];
+      const uint32_t tot = c4.x + c4.y + c4.z + c4.w;
+      uint32_t excl = wave_inclusive_scan(tot) - tot;  // keys in bins below 4 * lane
+      const uint32_t c[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c[e] > 0 && excl < rem && rem <= excl + c[e]) {
+          rs.digit = 4 * lane + e;
+          rs.rem = rem - excl;
+          rs.done = excl + c[e] == rem;
+        }
+        excl += c[e];
+      }
+      ((uint4*)rs.hist[hb ^ 1])[lane] = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
     uint32_t d = rs.digit;
@@ -129,7 +143,6 @@ __device__ void radix_select(KeyFn key_of, int N, int k, RadixScratch<NT>& rs, u
     if (kLargest) d = 255u - d;
     prefix |= (uint64_t)d << shift;
     mask |= 255ull << shift;
-    __syncthreads();
     if (done) break;
   }
 }
