@@ -127,13 +127,28 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(
     t.mask = mask;
     thr[prob] = t;
   }
+  // Chosen candidates per tile, counted in LDS (this workgroup owns every
+  // tile of its problem) and stored once per tile: device-scope atomics would
+  // serialise on the few tile counters when the threshold bin is crowded.
+  // Blocks of kTileBlock tiles bound the LDS for any history length.
+  constexpr int kTileBlock = 1024;
+  __shared__ uint32_t tcnt[kTileBlock];
   uint32_t* ch = chcount + (int64_t)h * NKT + kt_off[s];
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const uint64_t c = src[i];
-    if (radix_taken<true>(c, prefix, mask)) {
-      const int key = (int)(0xFFFFFFFFu - (uint32_t)c);
-      atomicAdd(&ch[key / kTopbKeys], 1u);
+  const int ntile = kt_off[s + 1] - kt_off[s];
+  for (int t0 = 0; t0 < ntile; t0 += kTileBlock) {
+    const int nt = min(kTileBlock, ntile - t0);
+    for (int i = threadIdx.x; i < nt; i += 256) tcnt[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const uint64_t c = src[i];
+      if (radix_taken<true>(c, prefix, mask)) {
+        const int tl = (int)(0xFFFFFFFFu - (uint32_t)c) / kTopbKeys - t0;
+        if (tl >= 0 && tl < nt) atomicAdd(&tcnt[tl], 1u);
+      }
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt; i += 256) ch[t0 + i] = tcnt[i];
+    __syncthreads();
   }
 }
 
