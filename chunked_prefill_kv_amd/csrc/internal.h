@@ -13,7 +13,7 @@ namespace quoka {
 // Tilings (all per sequence; tiles never straddle two sequences).
 constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
 constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup...
-constexpr int kScoreKeysSmall = 512; // ...or half as many when that fills the CUs better
+constexpr int kScoreKeysSmall = 256; // ...or a quarter as many when that fills the CUs better
 constexpr int kScoreMinBlocks = 1024; // scorer workgroups wanted (four per CU)
 constexpr int kTopbKeys = 2048;      // history keys per top-B workgroup
 constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
