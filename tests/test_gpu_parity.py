@@ -172,6 +172,9 @@ ORDER_CASES = {
     "pair_ragged": ([(1024, 2000), (500, 1500)], 32, 8, 128, "bf16", 16, 512),
     # 256 contiguous rows per workgroup; the last workgroup has one tile only
     "wide_odd": ([(1056, 600)] * 8, 32, 8, 128, "bf16", 8, 256),
+    # the same two orders with head_dim 64 (K/V tiles of 8 rows per 1 KB LDS piece)
+    "pair_odd_d64": ([(1056, 3000)], 32, 8, 64, "bf16", 16, 512),
+    "wide_odd_d64": ([(1056, 600)] * 8, 32, 8, 64, "bf16", 8, 256),
 }
 
 
