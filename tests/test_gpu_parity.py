@@ -175,6 +175,10 @@ ORDER_CASES = {
     # the same two orders with head_dim 64 (K/V tiles of 8 rows per 1 KB LDS piece)
     "pair_odd_d64": ([(1056, 3000)], 32, 8, 64, "bf16", 16, 512),
     "wide_odd_d64": ([(1056, 600)] * 8, 32, 8, 64, "bf16", 8, 256),
+    # GQA 7: 128-row tiles cut through a token's heads (paired order, 66 tiles)
+    "pair_g7": ([(1200, 3000)], 28, 4, 128, "bf16", 16, 512),
+    # one query head per KV head in the wide order, chunks of different lengths
+    "wide_g1": ([(4096, 300), (3000, 900)] * 4, 8, 8, 128, "bf16", 8, 128),
 }
 
 
