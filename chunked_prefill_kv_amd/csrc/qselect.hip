@@ -458,20 +458,36 @@ __global__ __launch_bounds__(kQselThreads) void qselect_kernel(
     constexpr int NDS = D / 32;
     bf16x8* dst = (bf16x8*)gsel + (int64_t)prob * (nq_pad / 16) * GH * NDS * 2 * 64;
     const int total = (nrows + 15) / 16 * GH * NDS * 64;
-    for (int v = threadIdx.x; v < total; v += NT) {
-      const int lane = v & 63, rest = v >> 6;  // rest = (qb * GH + j) * NDS + ds
-      const int ds = rest % NDS, j = (rest / NDS) % GH, qb = rest / NDS / GH;
-      const int row = qb * 16 + (lane & 15);
-      float x[8];
-      row8(row < nrows ? row : 0, j, ds * 32 + (lane >> 4) * 8, x);
-      bf16x8 hi, lo;
+    // U items per thread per round, every row read issued before the first
+    // conversion, so the reads of one round overlap
+    constexpr int U = 4;
+    for (int v0 = threadIdx.x; v0 < total; v0 += U * NT) {
+      float x[U][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = (bf16)x[e];
-        lo[e] = (bf16)(x[e] - (float)hi[e]);
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * NT;
+        if (v < total) {
+          const int lane = v & 63, rest = v >> 6;  // rest = (qb * GH + j) * NDS + ds
+          const int ds = rest % NDS, j = (rest / NDS) % GH, qb = rest / NDS / GH;
+          const int row = qb * 16 + (lane & 15);
+          row8(row < nrows ? row : 0, j, ds * 32 + (lane >> 4) * 8, x[u]);
+        }
       }
-      dst[(rest * 2 + 0) * 64 + lane] = hi;
-      dst[(rest * 2 + 1) * 64 + lane] = lo;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * NT;
+        if (v < total) {
+          const int lane = v & 63, rest = v >> 6;
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            hi[e] = (bf16)x[u][e];
+            lo[e] = (bf16)(x[u][e] - (float)hi[e]);
+          }
+          dst[(rest * 2 + 0) * 64 + lane] = hi;
+          dst[(rest * 2 + 1) * 64 + lane] = lo;
+        }
+      }
     }
   } else {
     float* dst = (float*)gsel + (int64_t)prob * nq_pad * GH * D;
