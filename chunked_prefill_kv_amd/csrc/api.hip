@@ -76,6 +76,14 @@ quoka_status ensure_lds(const Problem& p) {
   return QUOKA_OK;
 }
 
+// Scorer workgroups over all sequences for tiles of `keys` history keys.
+int64_t scorer_tiles(const quoka_shape& sh, int keys) {
+  int64_t n = 0;
+  for (int s = 0; s < sh.num_seqs; ++s)
+    n += ((int64_t)sh.cu_hist_host[s + 1] - sh.cu_hist_host[s] + keys - 1) / keys;
+  return n;
+}
+
 quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Problem* p) {
   if (!sh) return fail(QUOKA_EINVAL, "shape is null");
   if (sh->num_seqs < 1) return fail(QUOKA_EINVAL, "num_seqs=%d must be >= 1", sh->num_seqs);
@@ -110,24 +118,31 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
   p->cu_hist_h = sh->cu_hist_host;
   p->NQT = p->NSB = p->NKT = 0;
   p->maxC = p->maxL = 0;
-  int64_t nsb_small = 0;
   for (int s = 0; s < S; ++s) {
     const int64_t C = (int64_t)sh->cu_chunk_host[s + 1] - sh->cu_chunk_host[s];
     const int64_t L = (int64_t)sh->cu_hist_host[s + 1] - sh->cu_hist_host[s];
     if (C < 0 || L < 0)
       return fail(QUOKA_EINVAL, "cu offsets decrease at sequence %d", s);
     p->NQT += (C + kQprepTokens - 1) / kQprepTokens;
-    p->NSB += (L + kScoreKeys - 1) / kScoreKeys;
-    nsb_small += (L + kScoreKeysSmall - 1) / kScoreKeysSmall;
     p->NKT += (L + kTopbKeys - 1) / kTopbKeys;
     p->maxC = std::max<int>(p->maxC, (int)C);
     p->maxL = std::max<int>(p->maxL, (int)L);
   }
-  // smaller scorer tiles when the large ones would leave CUs with one workgroup
-  p->score_keys = kScoreKeys;
-  if (p->NSB * p->Hkv < kScoreMinBlocks) {
-    p->score_keys = kScoreKeysSmall;
-    p->NSB = nsb_small;
+  // Scorer tiles: one 64-key block per wave while that takes at most two
+  // rounds of workgroups; past that each wave streams several blocks with
+  // the next one in flight, in tiles just large enough for a single round
+  // (up to 2048 keys: beyond it the last workgroups' compute is exposed),
+  // and no larger than it takes to lower the workgroup count (short
+  // sequences).
+  p->score_keys = kScoreKeysMin;
+  p->NSB = scorer_tiles(*sh, p->score_keys);
+  if (p->NSB * p->Hkv > 2 * kScoreMaxBlocks) {
+    while (p->score_keys < kScoreKeysMax && p->NSB * p->Hkv > kScoreMaxBlocks) {
+      const int64_t n = scorer_tiles(*sh, p->score_keys * 2);
+      if (n == p->NSB && p->score_keys > kScoreKeysMin) break;
+      p->score_keys *= 2;
+      p->NSB = n;
+    }
   }
   p->TC = sh->cu_chunk_host[S];
   p->TL = sh->cu_hist_host[S];

@@ -12,9 +12,9 @@ namespace quoka {
 
 // Tilings (all per sequence; tiles never straddle two sequences).
 constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
-constexpr int kScoreKeys = 1024;     // history keys per scorer workgroup...
-constexpr int kScoreKeysSmall = 256; // ...or a quarter as many when that fills the CUs better
-constexpr int kScoreMinBlocks = 1024; // scorer workgroups wanted (four per CU)
+constexpr int kScoreKeysMin = 256;   // history keys per scorer workgroup: one block per wave...
+constexpr int kScoreKeysMax = 2048;  // ...up to eight blocks per wave, streamed
+constexpr int kScoreMaxBlocks = 512; // one round of scorer workgroups (two per CU)
 constexpr int kTopbKeys = 2048;      // history keys per top-B workgroup
 constexpr int kCandCap = 6144;       // candidates the top-B refinement keeps in LDS
 constexpr int kQselCap = 12288;      // chunk tokens whose cosines the query select stages in LDS
@@ -37,7 +37,7 @@ struct Problem {
   int64_t NQT, NSB, NKT;     // total qprep / scorer / top-B tiles over sequences
   int maxC, maxL;            // longest chunk, longest history
   int q_budget, kv_budget, nq_pad;
-  int score_keys;            // history keys per scorer workgroup (kScoreKeys or kScoreKeysSmall)
+  int score_keys;            // history keys per scorer workgroup (a power of two, 256..2048)
   int variant;               // quoka_variant
   int mode() const {
     return variant == QUOKA_VARIANT_DOT ? kModeDot

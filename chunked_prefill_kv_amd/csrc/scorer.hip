@@ -36,40 +36,46 @@ __device__ __forceinline__ void flush_hist(const uint32_t* lhist, uint32_t* __re
 //       contiguous bytes of one key row; 4 lanes cover 64 B of a row),
 //   C = [16 queries x 16 keys]; lane l holds key column l%16, so the max over
 //       queries is a per-lane max followed by two cross-lane steps.
-// One workgroup = 4 waves = up to KEYS keys of one (sequence, KV head).
-// Each wave streams 64-key blocks (4 MFMA blocks of 16 keys): the next block
-// is in flight while the current one is scored. Keys are read through a
-// buffer resource that ends at the sequence's last key, so reads past it
-// return zeros (those keys are never written).
-template <int D, int KEYS, int MODE>
+// One workgroup = 4 waves = NB * 256 keys of one (sequence, KV head). Wave w
+// scores the 64-key blocks w, w + 4, w + 8, ... of the tile; two blocks are
+// in flight per wave, and the block just scored is refilled with the one two
+// ahead. Keys are read through a buffer resource that covers exactly the
+// tile's keys, so reads past its last key return zeros without a memory
+// access. The block loop is unrolled at compile time and every load in it
+// is unconditional (only the scoring of blocks past the sequence's end is
+// skipped), so the compiler waits for exactly the 16 loads of the block in
+// hand rather than for every load in flight.
+template <int D, int NB, int MODE>
 __global__ __launch_bounds__(256) void scorer_mfma_kernel(
     const bf16* __restrict__ k_hist, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TL, int q_budget, int nq_pad, const bf16x8* __restrict__ gsel,
     float* __restrict__ scores, uint32_t* __restrict__ hist, int one_row, int G) {
+  constexpr int score_keys = NB * 256;
   constexpr int NDS = D / 32;                 // d-steps per key
-  constexpr int NIT = KEYS / 256;             // 64-key blocks per wave
   const int GH = MODE == kModeHeads ? G : 1;  // rows per kept token
   const int blk = blockIdx.x, h = blockIdx.y;
   const int32_t* sb_off = plan + (S + 1);
   const int s = upper_seq(sb_off, S, blk);
-  const int k_begin = (blk - sb_off[s]) * KEYS;
+  const int k_begin = (blk - sb_off[s]) * score_keys;
   const int h_off = cu_hist[s];
   const int L = cu_hist[s + 1] - h_off;
-  const int k_end = min(L, k_begin + KEYS);
+  const int k_end = min(L, k_begin + score_keys);
   const int n = min(one_row ? 1 : q_budget, cu_chunk[s + 1] - cu_chunk[s]);
   const int nqb = (n + 15) / 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int prob = s * Hkv + h;
+  const int first = k_begin + wave * 64;  // this wave's first key
 
-  // keys [0, k_end) of this (sequence, head); row stride Hkv * D
+  // keys [k_begin, k_end) of this (sequence, head); row stride Hkv * D
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2u;
   const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc(k_hist + ((int64_t)h_off * Hkv + h) * D, (uint32_t)(k_end - 1) * row_bytes + D * 2u);
+      make_rsrc(k_hist + ((int64_t)(h_off + k_begin) * Hkv + h) * D,
+                k_end > k_begin ? (uint32_t)(k_end - k_begin - 1) * row_bytes + D * 2u : 0u);
   const uint32_t lane_off = (uint32_t)(lane & 15) * row_bytes + (uint32_t)(lane >> 4) * 16u;
-  auto load = [&](int it, bf16x8 (&b)[4][NDS]) {
-    const uint32_t k0 = (uint32_t)(k_begin + it * 256 + wave * 64);
+  auto load = [=](int j, bf16x8 (&b)[4][NDS]) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)(wave * 64 + j * 256);  // tile-relative
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -82,35 +88,34 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
   // wave go out together, so the stream has no gap between the rounds.
   extern __shared__ char smem[];
   uint32_t* lhist = (uint32_t*)smem;                       // kScoreBins
-  bf16x8* lg = (bf16x8*)(smem + kScoreBins * 4);           // nqb * NDS * 2 * 64
+  bf16x8* lg = (bf16x8*)(smem + kScoreBins * 4);           // nqb * GH * NDS * 2 * 64
   const bf16x8* gsrc = gsel + (int64_t)prob * (nq_pad / 16) * GH * NDS * 2 * 64;
   const int nstage = nqb * GH * NDS * 2 * 64;
-  constexpr int kStageU = 8;  // 16-byte pieces per thread staged through registers
-  bf16x8 stg[kStageU];
+  constexpr int kStageU = 16;  // 16-byte pieces per thread staged through registers
+  {
+    bf16x8 stg[kStageU];
 #pragma unroll
-  for (int u = 0; u < kStageU; ++u) {
-    const int i = u * 256 + (int)threadIdx.x;
-    if (i < nstage) stg[u] = gsrc[i];
-  }
-  bf16x8 b0[4][NDS], b1[4][NDS];
-  for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
+    for (int u = 0; u < kStageU; ++u) {
+      const int i = u * 256 + (int)threadIdx.x;
+      if (i < nstage) stg[u] = gsrc[i];
+    }
+    for (int i = threadIdx.x; i < kScoreBins; i += 256) lhist[i] = 0u;
 #pragma unroll
-  for (int u = 0; u < kStageU; ++u) {
-    const int i = u * 256 + (int)threadIdx.x;
-    if (i < nstage) lg[i] = stg[u];
+    for (int u = 0; u < kStageU; ++u) {
+      const int i = u * 256 + (int)threadIdx.x;
+      if (i < nstage) lg[i] = stg[u];
+    }
   }
-  if (k_begin + wave * 64 < k_end) load(0, b0);
-  if (NIT > 1 && k_begin + 256 + wave * 64 < k_end) load(1, b1);
-  if (nstage > kStageU * 256)
+  if (nstage > kStageU * 256)  // only the per-head rows are this large
     block_copy<256, 8>(lg + kStageU * 256, gsrc + kStageU * 256, nstage - kStageU * 256);
+  bf16x8 b0[4][NDS], b1[4][NDS];
+  load(0, b0);
+  if constexpr (NB > 1) load(1, b1);
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    bf16x8 (&cur)[4][NDS] = (it & 1) ? b1 : b0;
-    const int k0 = k_begin + it * 256 + wave * 64;
-    if (k0 >= k_end) break;
+  auto score = [=](int j, bf16x8 (&cur)[4][NDS]) __attribute__((always_inline)) {
+    const int k0 = first + j * 256;
     float nsq[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int kb = 0; kb < 4 && MODE != kModeDot; ++kb) {
@@ -133,8 +138,8 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
       f32x4 acc[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) acc[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < GH; ++j) {  // per head rows accumulate: the sum over heads
-        const bf16x8* la = lg + (qb * GH + j) * NDS * 2 * 64 + lane;
+      for (int jh = 0; jh < GH; ++jh) {  // per head rows accumulate: the sum over heads
+        const bf16x8* la = lg + (qb * GH + jh) * NDS * 2 * 64 + lane;
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
           const bf16x8 ahi = la[(ds * 2 + 0) * 64];
@@ -168,8 +173,12 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
       srow[key] = sc;
       atomicAdd(&lhist[MODE == kModeDot ? score_bin_raw(sc) : score_bin(sc)], 1u);
     }
-    // the block just scored is refilled with the one two rounds ahead
-    if (it + 2 < NIT && k0 + 512 < k_end) load(it + 2, cur);
+  };
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    bf16x8 (&cur)[4][NDS] = (j & 1) ? b1 : b0;
+    if (first + j * 256 < k_end) score(j, cur);
+    if (j + 2 < NB) load(j + 2, cur);  // the block just scored is refilled two ahead
   }
   __syncthreads();
   flush_hist(lhist, hist, prob);
@@ -236,14 +245,11 @@ __global__ __launch_bounds__(256) void scorer_valu_kernel(
 
 hipError_t set_scorer_lds_limit(int bytes, int bytes_heads) {
   const void* fns[] = {
-      (const void*)scorer_mfma_kernel<128, kScoreKeys, kModeCos>,
-      (const void*)scorer_mfma_kernel<64, kScoreKeys, kModeCos>,
-      (const void*)scorer_mfma_kernel<128, kScoreKeysSmall, kModeCos>,
-      (const void*)scorer_mfma_kernel<64, kScoreKeysSmall, kModeCos>,
-      (const void*)scorer_mfma_kernel<128, kScoreKeys, kModeDot>,
-      (const void*)scorer_mfma_kernel<64, kScoreKeys, kModeDot>,
-      (const void*)scorer_mfma_kernel<128, kScoreKeysSmall, kModeDot>,
-      (const void*)scorer_mfma_kernel<64, kScoreKeysSmall, kModeDot>,
+#define QUOKA_SCORER_NB(D, M)                                                                 \
+  (const void*)scorer_mfma_kernel<D, 1, M>, (const void*)scorer_mfma_kernel<D, 2, M>,         \
+      (const void*)scorer_mfma_kernel<D, 4, M>, (const void*)scorer_mfma_kernel<D, 8, M>
+      QUOKA_SCORER_NB(128, kModeCos), QUOKA_SCORER_NB(64, kModeCos),
+      QUOKA_SCORER_NB(128, kModeDot), QUOKA_SCORER_NB(64, kModeDot),
       (const void*)scorer_valu_kernel<float, 128, kModeCos>,
       (const void*)scorer_valu_kernel<float, 64, kModeCos>,
       (const void*)scorer_valu_kernel<float, 128, kModeDot>,
@@ -252,10 +258,7 @@ hipError_t set_scorer_lds_limit(int bytes, int bytes_heads) {
     const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
   }
-  const void* fh[] = {(const void*)scorer_mfma_kernel<128, kScoreKeys, kModeHeads>,
-                      (const void*)scorer_mfma_kernel<64, kScoreKeys, kModeHeads>,
-                      (const void*)scorer_mfma_kernel<128, kScoreKeysSmall, kModeHeads>,
-                      (const void*)scorer_mfma_kernel<64, kScoreKeysSmall, kModeHeads>,
+  const void* fh[] = {QUOKA_SCORER_NB(128, kModeHeads), QUOKA_SCORER_NB(64, kModeHeads),
                       (const void*)scorer_valu_kernel<float, 128, kModeHeads>,
                       (const void*)scorer_valu_kernel<float, 64, kModeHeads>};
   for (const void* f : fh) {
@@ -263,6 +266,7 @@ hipError_t set_scorer_lds_limit(int bytes, int bytes_heads) {
         hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes_heads);
     if (e != hipSuccess) return e;
   }
+#undef QUOKA_SCORER_NB
   return hipSuccess;
 }
 
@@ -283,24 +287,27 @@ hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const W
   const int mode = p.mode();
   if (p.dtype == QUOKA_BF16) {
     const bf16x8* gsel = (const bf16x8*)(ws + w.gsel);
-    const bool small = p.score_keys == kScoreKeysSmall;
-#define QUOKA_SCORER(D, K, M)                                                                 \
-  hipLaunchKernelGGL((scorer_mfma_kernel<D, K, M>), grid, dim3(256), lds, st,                 \
+    const int nb = p.score_keys / 256;
+#define QUOKA_SCORER(D, NB, M)                                                                \
+  hipLaunchKernelGGL((scorer_mfma_kernel<D, NB, M>), grid, dim3(256), lds, st,                \
                      (const bf16*)k_hist, p.cu_chunk, p.cu_hist, plan, p.S, p.Hkv, p.TL,      \
                      p.q_budget, p.nq_pad, gsel, scores, hist, one, p.G)
-#define QUOKA_SCORER_K(D, M)                                                                  \
+#define QUOKA_SCORER_B(D, M)                                                                  \
   do {                                                                                        \
-    if (small) QUOKA_SCORER(D, kScoreKeysSmall, M); else QUOKA_SCORER(D, kScoreKeys, M);      \
+    if (nb == 1) QUOKA_SCORER(D, 1, M);                                                       \
+    else if (nb == 2) QUOKA_SCORER(D, 2, M);                                                  \
+    else if (nb == 4) QUOKA_SCORER(D, 4, M);                                                  \
+    else QUOKA_SCORER(D, 8, M);                                                               \
   } while (0)
 #define QUOKA_SCORER_M(D)                                                                     \
   do {                                                                                        \
-    if (mode == kModeDot) QUOKA_SCORER_K(D, kModeDot);                                        \
-    else if (mode == kModeHeads) QUOKA_SCORER_K(D, kModeHeads);                               \
-    else QUOKA_SCORER_K(D, kModeCos);                                                         \
+    if (mode == kModeDot) QUOKA_SCORER_B(D, kModeDot);                                        \
+    else if (mode == kModeHeads) QUOKA_SCORER_B(D, kModeHeads);                               \
+    else QUOKA_SCORER_B(D, kModeCos);                                                         \
   } while (0)
     if (p.D == 128) QUOKA_SCORER_M(128); else QUOKA_SCORER_M(64);
 #undef QUOKA_SCORER_M
-#undef QUOKA_SCORER_K
+#undef QUOKA_SCORER_B
 #undef QUOKA_SCORER
   } else {
     const float* gsel = (const float*)(ws + w.gsel);

@@ -36,6 +36,10 @@ CASES = {
     "bf16_decode_g4": ([(1, 3000), (1, 0), (2, 500), (1, 64)], 8, 2, 128, "bf16", 1, 256, {}),
     "bf16_decode_g8": ([(1, 1500), (1, 70)], 16, 2, 128, "bf16", 2, 1000, dict(scaled=True)),
     "bf16_decode_d64_g1": ([(1, 2000), (1, 100), (1, 1)], 2, 2, 64, "bf16", 1, 300, {}),
+    # scorer tiles of 1024 keys (four streamed blocks per wave), last tile partial
+    "bf16_scorer_tiles_1024": ([(64, 33000)], 8, 8, 128, "bf16", 16, 512, {}),
+    # scorer tiles of 512 keys: many short histories, some waves with one block
+    "bf16_scorer_tiles_512": ([(2, 300)] * 270, 4, 2, 128, "bf16", 2, 128, {}),
 }
 
 
