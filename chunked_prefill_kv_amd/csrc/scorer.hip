@@ -106,11 +106,15 @@ __global__ __launch_bounds__(256) void scorer_mfma_kernel(
       if (i < nstage) lg[i] = stg[u];
     }
   }
-  if (nstage > kStageU * 256)  // only the per-head rows are this large
-    block_copy<256, 8>(lg + kStageU * 256, gsrc + kStageU * 256, nstage - kStageU * 256);
   bf16x8 b0[4][NDS], b1[4][NDS];
   load(0, b0);
   if constexpr (NB > 1) load(1, b1);
+  // Only the per-head rows outgrow the register staging (at most 128 rows of
+  // d <= 128 otherwise); their rest is copied behind the first key loads.
+  if constexpr (MODE == kModeHeads) {
+    if (nstage > kStageU * 256)
+      block_copy<256, 8>(lg + kStageU * 256, gsrc + kStageU * 256, nstage - kStageU * 256);
+  }
   __syncthreads();
 
   float* srow = scores + (int64_t)h * TL + h_off;
