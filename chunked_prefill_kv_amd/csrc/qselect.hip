@@ -159,11 +159,15 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
 #pragma unroll
   for (int i = 0; i < kTokPerWave; ++i) {
     const int t = tw + i;
+    // the mean over the group: for a power-of-two G the product with 1/G is
+    // the same correctly rounded value as the quotient, at one instruction
+    if ((G & (G - 1)) == 0) {
+      const float inv_g = 1.0f / (float)G;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float v = acc[i][e];
-      v = rows_sum(v);
-      acc[i][e] = v / (float)G;
+      for (int e = 0; e < EPL; ++e) acc[i][e] = rows_sum(acc[i][e]) * inv_g;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[i][e] = rows_sum(acc[i][e]) / (float)G;
     }
     if (grp == 0 && t < C) {
       float* dst = g + ((int64_t)(c_off + t) * Hkv + h) * D + sub * EPL;
