@@ -150,6 +150,9 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
   if (p->TC * p->Hq > INT32_MAX || p->TL * p->Hkv > INT32_MAX)
     return fail(QUOKA_EUNSUPPORTED, "token totals too large");
   if ((int64_t)p->maxC * p->G > INT32_MAX) return fail(QUOKA_EUNSUPPORTED, "chunk too long");
+  // the fp64 re-ranking near the selection boundaries packs positions in 24 bits
+  if (p->maxC >= (1 << 24) || p->maxL >= (1 << 24))
+    return fail(QUOKA_EUNSUPPORTED, "a chunk or history of 2^24 tokens or more");
   // kernels address one sequence's rows through 32-bit buffer offsets
   const int64_t elem = sh->dtype == QUOKA_BF16 ? 2 : 4;
   const int64_t row = (int64_t)p->Hkv * p->D * elem;
@@ -180,6 +183,19 @@ quoka_status set_variant(int32_t variant, Problem* p) {
 
 }  // namespace
 
+ScoreBounds score_bounds(const Problem& p) {
+  const double u = 0x1p-24;
+  const bool bf = p.dtype == QUOKA_BF16;
+  const int GH = p.gh();
+  const double nt = (bf ? 2.0 : 1.0) * p.D * GH;  // products summed per score
+  // rows: g rounded to fp32 (2u, also covering the means of the one-row
+  // baselines); the per-head baseline's unit rows carry an fp32 norm
+  const double rows = (p.variant == QUOKA_VARIANT_PER_HEAD ? p.D / 2.0 + 3.0 : 2.0) * u;
+  const double row = rows + (bf ? 0x1p-18 * 1.01 : 0.0) + 2.0 * nt * u * 1.01;
+  const double eps = row + (p.D + 4.0) * u * 1.01;
+  return {(float)(row * 1.001), (float)(eps * 1.001)};
+}
+
 Workspace workspace_layout(const Problem& p) {
   Workspace w;
   size_t o = 0;
@@ -198,11 +214,17 @@ Workspace workspace_layout(const Problem& p) {
   w.scores = take((size_t)p.Hkv * p.TL * 4);
   w.zero_begin = o;
   w.hist = take(SH * kScoreBins * 4);
-  w.ccount = take(SH * 4);
   w.chcount = take((size_t)p.Hkv * p.NKT * 4);
+  // one bit per history key and head; the top-B write reads two words from
+  // any key's position, up to a tile past the last key
+  w.bits = take(((size_t)p.Hkv * p.TL + kTopbKeys + 64) / 32 * 4);
   w.zero_end = o;
   w.thr = take(SH * sizeof(Threshold));
   w.cand = take((size_t)p.Hkv * p.TL * 8);
+  w.cand2 = take((size_t)p.Hkv * p.TL * 8);
+  w.ctcount = take((size_t)p.Hkv * p.NKT * 4);
+  w.qkey = take((size_t)p.Hkv * p.TC * 8);
+  w.row0 = take(SH * p.D * 8);
   w.gtcount = take((size_t)p.Hkv * p.NKT * 4);
   w.select_end = o;
   w.selidx = take(SH * p.kv_budget * 4);
@@ -227,7 +249,7 @@ quoka_status run_select(const Problem& p, const Workspace& w, const void* q, con
   if ((rc = hip_check(launch_qprep(p, q, ws, w, qcos, qcos_opt != nullptr, qidx, sel_idx, st), "qprep", st)))
     return rc;
   if ((rc = hip_check(launch_scorer(p, k_hist, ws, w, scores, st), "scorer", st))) return rc;
-  return hip_check(launch_topb(p, ws, w, scores, sel_idx, st), "topb", st);
+  return hip_check(launch_topb(p, q, k_hist, qidx, ws, w, scores, sel_idx, st), "topb", st);
 }
 
 #define QUOKA_NEED(ptr, total)                                                          \

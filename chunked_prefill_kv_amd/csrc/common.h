@@ -91,6 +91,39 @@ __device__ __forceinline__ uint32_t row16_sum(uint32_t v) {
   v += dpp_u32<kDppMirror>(v);
   return v;
 }
+// Sum over each aligned group of four lanes (the same bits in all four).
+__device__ __forceinline__ double quad_sum(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  return v;
+}
+
+// Sum over each aligned group of eight lanes.
+__device__ __forceinline__ double oct_sum(double v) {
+  v = quad_sum(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  return v;
+}
+
+// Sum of a double with its partner lane l ^ 16 (resp. l ^ 32), the same bits
+// in both lanes.
+__device__ __forceinline__ double pair16_sum(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint32_t a0, b0, a1, b1;
+  swap16((uint32_t)u, a0, b0);
+  swap16((uint32_t)(u >> 32), a1, b1);
+  return __longlong_as_double((long long)(((uint64_t)a1 << 32) | a0)) +
+         __longlong_as_double((long long)(((uint64_t)b1 << 32) | b0));
+}
+__device__ __forceinline__ double pair32_sum(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint32_t a0, b0, a1, b1;
+  swap32((uint32_t)u, a0, b0);
+  swap32((uint32_t)(u >> 32), a1, b1);
+  return __longlong_as_double((long long)(((uint64_t)a1 << 32) | a0)) +
+         __longlong_as_double((long long)(((uint64_t)b1 << 32) | b0));
+}
+
 // Sum / max of the four lanes l, l ^ 16, l ^ 32, l ^ 48.
 __device__ __forceinline__ float rows_sum(float v) {
   uint32_t a, b;
@@ -144,7 +177,23 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
   return x;
 }
 
+__device__ __forceinline__ uint32_t row16_min(uint32_t v) {
+  v = min(v, dpp_u32<kDppXor1>(v));
+  v = min(v, dpp_u32<kDppXor2>(v));
+  v = min(v, dpp_u32<kDppHalfMirror>(v));
+  v = min(v, dpp_u32<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t rows_min(uint32_t v) {
+  uint32_t a, b;
+  swap16(v, a, b);
+  v = min(a, b);
+  swap32(v, a, b);
+  return min(a, b);
+}
+
 // ---- wave reductions (64 lanes, result in every lane) --------------------
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) { return rows_min(row16_min(v)); }
 __device__ __forceinline__ float wave_sum(float v) { return rows_sum(row16_sum(v)); }
 __device__ __forceinline__ double wave_sum(double v) { return rows_sum(row16_sum(v)); }
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return rows_sum(row16_sum(v)); }
@@ -156,6 +205,43 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of float_order_key (the key of -0 decodes to +0).
+__device__ __forceinline__ float float_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The same monotone map for doubles: a < b <=> key(a) < key(b), -0 == +0.
+__device__ __forceinline__ uint64_t double_order_key(double x) {
+  if (x == 0.0) x = 0.0;
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double double_from_order_key(uint64_t k) {
+  return __longlong_as_double((long long)((k & 0x8000000000000000ull) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+
+// Keys of the exact (fp64) re-evaluation near a selection boundary. Indices
+// below 2^24 (the host rejects longer sequences); the value keeps the top
+// bits of its double order key: 40 for history keys (sign, exponent and 28
+// mantissa bits: two values closer than 2^-28 relative share a key and the
+// lower index wins), 38 behind a two-bit class for chunk tokens.
+constexpr int kExactIdxBits = 24;
+constexpr uint32_t kExactIdxMask = (1u << kExactIdxBits) - 1u;
+// larger is better: value desc, then index asc
+__device__ __forceinline__ uint64_t exact_key_desc(double v, int idx) {
+  return ((double_order_key(v) >> kExactIdxBits) << kExactIdxBits) |
+         (uint64_t)(kExactIdxMask - (uint32_t)idx);
+}
+__device__ __forceinline__ int exact_key_index_desc(uint64_t k) {
+  return (int)(kExactIdxMask - (uint32_t)(k & kExactIdxMask));
+}
+// smaller is better: class (0 sure in, 1 decided by value, 2 sure out), then
+// value asc, then index asc
+__device__ __forceinline__ uint64_t class_key_asc(uint32_t cls, double v, int idx) {
+  const uint64_t val = cls == 1u ? (double_order_key(v) >> (64 - 38)) : 0ull;
+  return ((uint64_t)cls << 62) | (val << kExactIdxBits) | (uint64_t)(uint32_t)idx;
 }
 
 // Linear histogram bin of a score in [-1, 1] (cosine-derived scores are
@@ -172,6 +258,29 @@ __device__ __forceinline__ int score_bin(float s) {
 // binade), which only makes the top-B refinement see more candidates.
 __device__ __forceinline__ int score_bin_raw(float s) { return (int)(float_order_key(s) >> 21); }
 static_assert(kScoreBins == 2048, "score_bin_raw yields 11 bits");
+
+// Eight consecutive row elements in their storage type, read as fp64 (bf16
+// and fp32 convert exactly).
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *(const bf16x8*)p; }
+  __device__ __forceinline__ double operator[](int e) const { return (double)(float)v[e]; }
+};
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *(const float4*)p;
+    b = *(const float4*)(p + 4);
+  }
+  __device__ __forceinline__ double operator[](int e) const {
+    return e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : e == 3 ? a.w
+         : e == 4 ? b.x : e == 5 ? b.y : e == 6 ? b.z : b.w;
+  }
+};
 
 // ---- buffer loads ----------------------------------------------------------
 // Raw buffer resource over [p, p + nbytes): loads at byte offsets >= nbytes

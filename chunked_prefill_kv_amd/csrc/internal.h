@@ -64,23 +64,47 @@ struct Workspace {
   size_t scores;    // float [Hkv, TL]
   size_t hist;      // uint32 [S, Hkv, kScoreBins]
   size_t thr;       // Threshold [S, Hkv]
-  size_t ccount;    // uint32 [S, Hkv] candidate counts
-  size_t cand;      // uint64 [Hkv, TL] candidates
+  size_t ctcount;   // uint32 [Hkv, NKT] candidates per tile
+  size_t cand;      // uint64 [Hkv, TL] candidates, each tile's in its own key range
+  size_t cand2;     // uint64 [Hkv, TL] a problem's candidates gathered (beyond the LDS)
   size_t gtcount;   // uint32 [Hkv, NKT] keys above the threshold bin per tile
   size_t chcount;   // uint32 [Hkv, NKT] chosen candidates per tile
+  size_t bits;      // uint32 bitmap over [Hkv, TL]: chosen candidates
+  size_t qkey;      // uint64 [Hkv, TC] tokens re-ranked in fp64
+  size_t row0;      // double [S, Hkv, D] the one-row baselines' row in fp64
   size_t selidx;    // int32 [S, Hkv, B]  (prefill path)
   size_t select_end, total;
   size_t zero_begin, zero_end;  // [hist .. chcount] region cleared per call
 };
 
 struct Threshold {
-  int32_t bstar;        // bin holding the B_eff-th score; -1 = keep everything
-  int32_t above;        // keys in bins above bstar
-  int32_t need;         // keys still to take from bin bstar
-  int32_t pad;
-  uint64_t prefix;      // chosen candidates: (cand_key & mask) >= prefix
-  uint64_t mask;
+  int32_t bstar;           // bin holding the B_eff-th score; -1 = keep everything
+  int32_t above;           // keys in bins above bin_hi (all kept)
+  int32_t need;            // keys to choose among the candidates
+  int32_t bin_lo, bin_hi;  // candidate window of bins around bstar
+  int32_t pad[3];
 };
+
+// |fp32 cosine to the mean query - fp64 cosine|. The stored g is the fp64
+// mean of unit head rows rounded once to fp32 (relative error 2^-24 per
+// element, so the cosine moves by at most 2^-24); the fp64 products with the
+// fp64 mean query add ~1e-13 and the quotient's rounding to fp32 2^-24: 2^-23
+// with a factor of two to spare.
+constexpr float kQcosErr = 0x1p-22f;
+
+// Error bounds of the scorer's fp32 values against the fp64 definition:
+//   eps_row bounds |fp32 product - fp64 product| of one kept row with a key,
+//           in units of |k| (rows have norm <= 1): the row's own rounding to
+//           fp32, the hi/lo bf16 split (residual <= 2^-18 |g| per element)
+//           and the fp32 accumulation of nt products (at most nt roundings,
+//           each <= 2^-23 relative to the running sum whether the adder
+//           rounds to nearest or toward zero);
+//   eps     bounds |fp32 score - fp64 score|: eps_row plus |k| from a sum of
+//           d squares, its square root and the quotient.
+struct ScoreBounds {
+  float eps_row, eps;
+};
+ScoreBounds score_bounds(const Problem& p);
 
 Workspace workspace_layout(const Problem& p);
 
@@ -100,8 +124,9 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
 size_t scorer_lds_bytes(const Problem& p);
 hipError_t launch_scorer(const Problem& p, const void* k_hist, char* ws, const Workspace& w,
                          float* scores, hipStream_t st);
-hipError_t launch_topb(const Problem& p, char* ws, const Workspace& w, const float* scores,
-                       int32_t* sel_idx, hipStream_t st);
+hipError_t launch_topb(const Problem& p, const void* q, const void* k_hist, const int32_t* qidx,
+                       char* ws, const Workspace& w, const float* scores, int32_t* sel_idx,
+                       hipStream_t st);
 hipError_t launch_gather(const Problem& p, const void* k_hist, const void* v_hist,
                          const int32_t* sel_idx, void* k_sel, void* v_sel, hipStream_t st);
 // sel == nullptr: history rows are k_sel / v_sel [S, Hkv, kv_budget, D];

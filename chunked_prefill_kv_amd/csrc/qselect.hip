@@ -56,33 +56,36 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ c
 // K1a: g_t = mean_j unit(q_{t,j}) over the G query heads of KV head h, for a
 // tile of 64 tokens; also the tile's fp64 sum of g (for the mean query).
 // 16 waves; each wave owns 4 tokens and issues all their row loads before
-// reducing. Lanes work in groups of 16 on one head row (4 rows/instruction).
+// reducing. A head row is spread over D / 4 lanes (4 elements each), so one
+// load instruction covers 256 / D rows; the arithmetic is fp64.
 // ---------------------------------------------------------------------------
 constexpr int kQprepThreads = 1024;
 constexpr int kQprepWaves = kQprepThreads / 64;
 constexpr int kTokPerWave = kQprepTokens / kQprepWaves;  // 4
 
-// EPL consecutive elements as fp32, with 16-byte (or 8-byte) vector loads.
-template <typename T, int EPL>
-__device__ __forceinline__ void load_row(const T* __restrict__ p, float (&x)[EPL]) {
+// 4 consecutive elements as fp32 (one 8- or 16-byte load).
+template <typename T>
+__device__ __forceinline__ void load4(const T* __restrict__ p, float (&x)[4]) {
   if constexpr (sizeof(T) == 2) {
-    static_assert(EPL % 4 == 0, "bf16 rows load 4 or 8 elements");
-    if constexpr (EPL == 8) {
-      const bf16x8 v = *(const bf16x8*)p;
+    const bf16x4 v = *(const bf16x4*)p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
-    } else {
-      const bf16x4 v = *(const bf16x4*)p;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
-    }
+    for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
   } else {
-#pragma unroll
-    for (int e = 0; e < EPL; e += 4) {
-      const float4 v = *(const float4*)(p + e);
-      x[e] = v.x; x[e + 1] = v.y; x[e + 2] = v.z; x[e + 3] = v.w;
-    }
+    const float4 v = *(const float4*)p;
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
   }
+}
+
+// Sum over the RL lanes of one head row (aligned groups of RL = 16 or 32).
+template <int RL>
+__device__ __forceinline__ double head_row_sum(double v) {
+  v = row16_sum(v);
+  return RL == 32 ? pair16_sum(v) : v;
+}
+// Sum over the 64 / RL head rows of one load instruction (lanes l, l + RL, ...).
+template <int RL>
+__device__ __forceinline__ double head_group_sum(double v) {
+  return RL == 32 ? pair32_sum(v) : rows_sum(v);
 }
 
 template <typename T, int D>
@@ -91,7 +94,9 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     const int32_t* __restrict__ cu_hist, int S, int Hq, int Hkv, int G, float* __restrict__ g,
     double* __restrict__ gpart, int score_keys, int32_t* __restrict__ plan,
     uint4* __restrict__ zero, int64_t nzero16) {
-  constexpr int EPL = D / 16;  // elements per lane
+  constexpr int EPL = 4;       // elements per lane
+  constexpr int RL = D / EPL;  // lanes per head row: 32 or 16
+  constexpr int RPI = 64 / RL; // head rows per load instruction
   const int tile = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the plan and the cleared counters are for the later kernels
@@ -120,16 +125,19 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
   }
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;
-  const int grp = lane >> 4, sub = lane & 15;
+  const int grp = lane / RL, sub = lane % RL;
   const int tw = (tile - t_base) * kQprepTokens + wave * kTokPerWave;
 
-  float acc[kTokPerWave][EPL];
+  // the unit head rows and their mean over the group in fp64, so that the
+  // tile sums (hence the mean query) and the stored g (rounded once to fp32)
+  // are the fp64 values up to rounding
+  double acc[kTokPerWave][EPL];
 #pragma unroll
   for (int i = 0; i < kTokPerWave; ++i)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
+    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.0;
 
-  for (int j0 = 0; j0 < G; j0 += 4) {
+  for (int j0 = 0; j0 < G; j0 += RPI) {
     const int j = j0 + grp;
     float x[kTokPerWave][EPL];
 #pragma unroll
@@ -138,19 +146,19 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
       const bool ok = t < C && j < G;
       const T* row = q + ((int64_t)(c_off + (ok ? t : 0)) * Hq + (int64_t)h * G + (ok ? j : 0)) * D +
                      sub * EPL;
-      load_row<T, EPL>(row, x[i]);
+      load4<T>(row, x[i]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[i][e] = ok ? x[i][e] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kTokPerWave; ++i) {
-      float ss = 0.f;
+      double ss = 0.0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ss = fmaf(x[i][e], x[i][e], ss);
-      ss = row16_sum(ss);
-      const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+      for (int e = 0; e < EPL; ++e) ss = fma((double)x[i][e], (double)x[i][e], ss);
+      ss = head_row_sum<RL>(ss);
+      const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] = fmaf(x[i][e], inv, acc[i][e]);
+      for (int e = 0; e < EPL; ++e) acc[i][e] = fma((double)x[i][e], inv, acc[i][e]);
     }
   }
   double part[EPL];
@@ -162,20 +170,19 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     // the mean over the group: for a power-of-two G the product with 1/G is
     // the same correctly rounded value as the quotient, at one instruction
     if ((G & (G - 1)) == 0) {
-      const float inv_g = 1.0f / (float)G;
+      const double inv_g = 1.0 / (double)G;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] = rows_sum(acc[i][e]) * inv_g;
+      for (int e = 0; e < EPL; ++e) acc[i][e] = head_group_sum<RL>(acc[i][e]) * inv_g;
     } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] = rows_sum(acc[i][e]) / (float)G;
+      for (int e = 0; e < EPL; ++e) acc[i][e] = head_group_sum<RL>(acc[i][e]) / (double)G;
     }
     if (grp == 0 && t < C) {
       float* dst = g + ((int64_t)(c_off + t) * Hkv + h) * D + sub * EPL;
+      *(float4*)dst = make_float4((float)acc[i][0], (float)acc[i][1], (float)acc[i][2],
+                                  (float)acc[i][3]);
 #pragma unroll
-      for (int e = 0; e < EPL; e += 4)
-        *(float4*)(dst + e) = make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) part[e] += (double)acc[i][e];
+      for (int e = 0; e < EPL; ++e) part[e] += acc[i][e];
     }
   }
   __shared__ double red[kQprepWaves][D];
@@ -194,24 +201,67 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
 
 // ---------------------------------------------------------------------------
 // K2: keep the N_q,eff tokens with the lowest cosine (ties to the lower
-// token) by an exact radix select over the unique keys
-// (order_key(c) << 32 | t), and write them ascending to out and kept.
-// Returns N_q,eff.
+// token), as the fp64 cosines order them, and write them ascending to out
+// and kept. Returns N_q,eff.
+//
+// src holds fp32 cosines within err of the fp64 values. An exact radix select
+// over the unique keys (order_key(c) << 32 | t) decides every token except
+// those within 2 err of the N_q,eff-th value: if that band holds more tokens
+// than the places left for it, their cosines are recomputed in fp64
+// (exact_cos, one wave per token) and the selection is redone over class
+// keys (tokens surely in, then the band by fp64 value, then the rest) kept
+// in kbuf [C].
 // ---------------------------------------------------------------------------
-template <int NT>
+template <int NT, typename ExactFn>
 __device__ int select_tokens(int C, int q_budget, const float* __restrict__ src, float* cs,
-                             RadixScratch<NT>& rs, int32_t* __restrict__ out, int32_t* kept) {
+                             RadixScratch<NT>& rs, float err, uint64_t* __restrict__ kbuf,
+                             ExactFn exact_cos, int32_t* __restrict__ out, int32_t* kept) {
   const int n = min(q_budget, C);
   if (C <= kQselCap && src != cs) {
     block_copy<NT, 4>(cs, src, C);
     src = cs;
   }
   __syncthreads();
-  auto key_of = [&](int t) -> uint64_t {
+  auto approx_key = [&](int t) -> uint64_t {
     return ((uint64_t)float_order_key(src[t]) << 32) | (uint32_t)t;
   };
   uint64_t prefix = ~0ull, mask = ~0ull;  // keep everything when n == C
-  if (n < C) radix_select<false, NT>(key_of, C, n, rs, prefix, mask);
+  bool use_k = false;
+  if (n < C) {
+    radix_select<false, NT>(approx_key, C, n, rs, prefix, mask);
+    // cn, the n-th lowest fp32 cosine: when every token left out lies more
+    // than 2 err above it, the fp32 selection is the fp64 one
+    uint32_t kn = 0u, kout = ~0u;
+    for (int t = threadIdx.x; t < C; t += NT) {
+      const uint64_t k = approx_key(t);
+      if (radix_taken<false>(k, prefix, mask)) kn = max(kn, (uint32_t)(k >> 32));
+      else kout = min(kout, (uint32_t)(k >> 32));
+    }
+    kn = block_max<NT>(kn, rs);
+    kout = block_min<NT>(kout, rs);
+    const double cn = (double)float_from_order_key(kn);
+    const double lo = cn - 2.0 * (double)err, hi = cn + 2.0 * (double)err;
+    if ((double)float_from_order_key(kout) <= hi) {
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      for (int t0 = wave * 64; t0 < C; t0 += NT) {
+        const int t = t0 + lane;
+        const double c = t < C ? (double)src[t] : 0.0;
+        const bool band = t < C && c >= lo && c <= hi;
+        if (t < C && !band) kbuf[t] = class_key_asc(c < lo ? 0u : 2u, 0.0, t);
+        uint64_t m = __ballot(band);
+        while (m) {
+          const int l = __ffsll((unsigned long long)m) - 1;
+          m &= m - 1;
+          const double ce = exact_cos(t0 + l);
+          if (lane == 0) kbuf[t0 + l] = class_key_asc(1u, ce, t0 + l);
+        }
+      }
+      __syncthreads();
+      radix_select<false, NT>([&](int t) { return kbuf[t]; }, C, n, rs, prefix, mask);
+      use_k = true;
+    }
+  }
+  auto key_of = [&](int t) -> uint64_t { return use_k ? kbuf[t] : approx_key(t); };
 
   // ascending compaction of the kept tokens
   const int per = (C + NT - 1) / NT;
@@ -228,6 +278,56 @@ __device__ int select_tokens(int C, int q_budget, const float* __restrict__ src,
   }
   for (int i = n + threadIdx.x; i < q_budget; i += NT) out[i] = -1;
   return n;
+}
+
+// The fp64 cosine of token row `tok` (c_off + t) of KV head h to the chunk's
+// mean query, by one wave (the value in every lane): g = mean_j unit(q_j)
+// over the group's heads, M = (1/C) sum of the fp64 tile sums of g (tiles
+// [k0, k1) of the chunk).
+template <typename T, int D>
+__device__ double exact_token_cos(const T* __restrict__ q, int64_t tok, int Hq, int h, int G,
+                                  const double* __restrict__ gpart, int Hkv, int k0, int k1,
+                                  int C) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  double m[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) m[e] = 0.0;
+  for (int k = k0; k < k1; ++k)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) m[e] += gpart[((int64_t)k * Hkv + h) * D + lane * EPL + e];
+  double g[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    m[e] /= (double)C;
+    g[e] = 0.0;
+  }
+  for (int j = 0; j < G; ++j) {
+    const T* row = q + (tok * Hq + (int64_t)h * G + j) * D + lane * EPL;
+    double x[EPL], ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      x[e] = (double)to_f32(row[e]);
+      ss = fma(x[e], x[e], ss);
+    }
+    ss = wave_sum(ss);
+    const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) g[e] = fma(x[e], inv, g[e]);
+  }
+  double dot = 0.0, gg = 0.0, mm = 0.0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    g[e] /= (double)G;
+    dot = fma(g[e], m[e], dot);
+    gg = fma(g[e], g[e], gg);
+    mm = fma(m[e], m[e], mm);
+  }
+  dot = wave_sum(dot);
+  gg = wave_sum(gg);
+  mm = wave_sum(mm);
+  const double den = sqrt(mm) * sqrt(gg);
+  return den > 0.0 ? dot / den : 0.0;
 }
 
 // 8 consecutive elements of a row as fp32.
@@ -352,7 +452,8 @@ __global__ __launch_bounds__(kQselThreads) void qselect_kernel(
     int G, int64_t TC, const float* __restrict__ g, const double* __restrict__ gpart,
     const float* __restrict__ qcos, int q_budget, int nq_pad, int variant,
     int32_t* __restrict__ qidx, void* __restrict__ gsel, int kv_budget,
-    int32_t* __restrict__ sel_idx) {
+    int32_t* __restrict__ sel_idx, float cos_err, uint64_t* __restrict__ qkey,
+    double* __restrict__ row0) {
   using T = typename std::conditional<kMfma, bf16, float>::type;
   constexpr int NT = kQselThreads;
   const T* q = (const T*)qv;
@@ -368,6 +469,7 @@ __global__ __launch_bounds__(kQselThreads) void qselect_kernel(
   __shared__ int32_t kept[QUOKA_MAX_Q_BUDGET];
   __shared__ RadixScratch<NT> rs;
   __shared__ float mrow[D];
+  __shared__ double wpart[kQselThreads / 64][D];
   __shared__ float inv_norm[kMaxHeadRows];
   int32_t* out = qidx + (int64_t)prob * q_budget;
   const bool one = variant == QUOKA_VARIANT_MEAN_QUERIES || variant == QUOKA_VARIANT_MEAN_QUERY;
@@ -383,27 +485,82 @@ __global__ __launch_bounds__(kQselThreads) void qselect_kernel(
       double a = 0.0;
       for (int k = qt_off[s]; k < qt_off[s + 1]; ++k)
         a += gpart[((int64_t)k * Hkv + h) * D + threadIdx.x];
-      mrow[threadIdx.x] = (float)(a / (double)C);
+      a /= (double)C;
+      mrow[threadIdx.x] = (float)a;
+      row0[(int64_t)prob * D + threadIdx.x] = a;
     }
   } else {
     const float* src = qcos + (int64_t)h * TC + c_off;
-    if (variant == QUOKA_VARIANT_GLOBAL) {  // C <= kQselCap (checked on the host)
+    const bool global = variant == QUOKA_VARIANT_GLOBAL;
+    // the fp32 cosines are within cos_err of the fp64 ones; the head average
+    // of the cross-head baseline adds its own fp32 sums and quotient
+    float err = cos_err;
+    if (global) {  // C <= kQselCap (checked on the host)
       for (int t = threadIdx.x; t < C; t += NT) {
         float a = 0.f;
         for (int hh = 0; hh < Hkv; ++hh) a += qcos[(int64_t)hh * TC + c_off + t];
         cs[t] = a / (float)Hkv;
       }
       src = cs;
+      err += (float)(Hkv + 2) * 0x1p-24f;
     }
-    n = select_tokens<NT>(C, q_budget, src, cs, rs, out, kept);
+    const int k0 = plan[s], k1 = plan[s + 1];  // this chunk's query-prep tiles
+    auto exact_cos = [&](int t) -> double {
+      if (!global) return exact_token_cos<T, D>(q, c_off + t, Hq, h, G, gpart, Hkv, k0, k1, C);
+      double a = 0.0;
+      for (int hh = 0; hh < Hkv; ++hh)
+        a += exact_token_cos<T, D>(q, c_off + t, Hq, hh, G, gpart, Hkv, k0, k1, C);
+      return a / (double)Hkv;
+    };
+    n = select_tokens<NT>(C, q_budget, src, cs, rs, err, qkey + (int64_t)h * TC + c_off,
+                          exact_cos, out, kept);
     if (n == 0) return;  // empty chunk: the scorer writes zero scores
     __syncthreads();
     if (variant == QUOKA_VARIANT_MEAN_QUERIES) {
+      // the mean over the kept tokens of g_t in fp64, from the query rows:
+      // quad u (four lanes, D / 4 dims each) takes tokens u, u + 128, ...
+      constexpr int QE = D / 4, QL = QE / 8;
+      const int quad = threadIdx.x >> 2, ql = threadIdx.x & 3;
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      double gs[QE];
+#pragma unroll
+      for (int e = 0; e < QE; ++e) gs[e] = 0.0;
+      for (int r = quad; r < n; r += NT / 4) {
+        const T* qt = q + ((int64_t)(c_off + kept[r]) * Hq + (int64_t)h * G) * D + ql * QE;
+        for (int j = 0; j < G; ++j) {
+          Raw8<T> x[QL];
+#pragma unroll
+          for (int u = 0; u < QL; ++u) x[u].load(qt + (int64_t)j * D + u * 8);
+          double xx = 0.0;
+#pragma unroll
+          for (int u = 0; u < QL; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xx = fma(x[u][e], x[u][e], xx);
+          xx = quad_sum(xx);
+          const double inv = xx > 0.0 ? 1.0 / sqrt(xx) : 0.0;
+#pragma unroll
+          for (int u = 0; u < QL; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gs[u * 8 + e] = fma(x[u][e], inv, gs[u * 8 + e]);
+        }
+      }
+      // the wave's 16 quads (row_ror 4 and 8 inside each row, then the four
+      // rows), then the waves through LDS
+#pragma unroll
+      for (int e = 0; e < QE; ++e) {
+        double v = gs[e];
+        v += dpp_f64<0x124>(v);
+        v += dpp_f64<0x128>(v);
+        v = rows_sum(v);
+        if (lane < 4) wpart[wave][ql * QE + e] = v;
+      }
+      __syncthreads();
       if (threadIdx.x < D) {
         double a = 0.0;
-        for (int r = 0; r < n; ++r)
-          a += (double)g[((int64_t)(c_off + kept[r]) * Hkv + h) * D + threadIdx.x];
-        mrow[threadIdx.x] = (float)(a / (double)n);
+        for (int w2 = 0; w2 < NT / 64; ++w2) a += wpart[w2][threadIdx.x];
+        a /= (double)n * (double)G;
+        mrow[threadIdx.x] = (float)a;
+        row0[(int64_t)prob * D + threadIdx.x] = a;
       }
     } else if (variant == QUOKA_VARIANT_PER_HEAD) {  // n * G <= kMaxHeadRows (host check)
       for (int i = threadIdx.x; i < n * G; i += NT) {
@@ -552,7 +709,8 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
   hipLaunchKernelGGL((qselect_kernel<D, M>), sgrid, dim3(kQselThreads), 0, st, q, p.cu_chunk,   \
                      p.cu_hist,                                                               \
                      plan, p.Hq, p.Hkv, p.G, p.TC, g, gpart, qcos, p.q_budget, p.nq_pad,      \
-                     p.variant, qidx, (void*)(ws + w.gsel), p.kv_budget, sel_idx)
+                     p.variant, qidx, (void*)(ws + w.gsel), p.kv_budget, sel_idx, kQcosErr,   \
+                     (uint64_t*)(ws + w.qkey), (double*)(ws + w.row0))
   const bool mfma = p.dtype == QUOKA_BF16;
   if (p.D == 128) { if (mfma) QUOKA_QSEL(128, true); else QUOKA_QSEL(128, false); }
   else            { if (mfma) QUOKA_QSEL(64, true);  else QUOKA_QSEL(64, false); }

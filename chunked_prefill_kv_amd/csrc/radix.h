@@ -48,6 +48,24 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, RadixScratch<NT>& rs) 
   return t;
 }
 
+// Minimum / maximum of one value per thread over the block.
+template <int NT>
+__device__ __forceinline__ uint32_t block_min(uint32_t v, RadixScratch<NT>& rs) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_min(v);
+  if (lane == 0) rs.wsum[w] = v;
+  __syncthreads();
+  uint32_t t = ~0u;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) t = min(t, rs.wsum[i]);
+  __syncthreads();
+  return t;
+}
+template <int NT>
+__device__ __forceinline__ uint32_t block_max(uint32_t v, RadixScratch<NT>& rs) {
+  return ~block_min<NT>(~v, rs);
+}
+
 // Exact selection of the k smallest (kLargest = false) or k largest
 // (kLargest = true) of N unique 64-bit keys key_of(0..N-1), 1 <= k < N.
 // Result: the selected keys are exactly those with

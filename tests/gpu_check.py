@@ -4,16 +4,18 @@ check every stage against the fp64 oracle.
 The check is stage-conditioned: each oracle stage after the first runs on the
 GPU's own result of the stage before (its kept queries for scoring, its kept
 keys for attention), so a legitimate near-tie in one stage cannot cascade
-into differences in later ones. Index sets must match exactly except for
-members whose value lies inside the tie band around the boundary value:
+into differences in later ones. Index sets must match the oracle's exactly
+except for members whose oracle value lies within 1e-5 relative of the
+boundary value (the stated selection tolerance):
 
-* kept queries: |c_t - c_(N_q)| <= QCOS_BAND. The GPU computes c in fp32
-  from an fp64 mean query; the measured error is QCOS_TOL, so two tokens whose
-  cosines differ by less than 2 * QCOS_TOL may be ordered either way.
-* kept keys: |s_i - s_(B)| <= 1e-5 * |s_(B)| (the stated selection
-  tolerance), widened to 2 * SCORE_TOL when s_(B) is that close to 0.
-Beyond the bands, the GPU's selections must be exactly the oracle's selection
-rule applied to the GPU's own cosines and scores (same rule, bit-exact).
+* kept queries: |c_t - c_(N_q)| <= 1e-5 |c_(N_q)|;
+* kept keys:    |s_i - s_(B)|   <= 1e-5 |s_(B)|.
+
+The library meets this by construction: its fp32 cosines and scores are
+within stated bounds (QCOS_TOL, score_bound) of the fp64 values, and every
+member within twice that bound of its fp32 boundary value is re-evaluated in
+fp64 before the choice. So the GPU's selection must also equal the selection
+rule applied to its own fp32 values, except inside that re-evaluation band.
 """
 from __future__ import annotations
 
@@ -25,11 +27,26 @@ import torch
 import chunked_prefill_kv_amd as cpk
 import oracle
 
-QCOS_TOL = 1e-6          # |c_gpu - c_oracle|
-QCOS_BAND = 2 * QCOS_TOL
-SCORE_TOL = {"fp32": 1e-6, "bf16": 2e-6}   # |s_gpu - s_oracle|
-SEL_REL_BAND = 1e-5
+QCOS_TOL = 2.0 ** -22     # |c_gpu - c_oracle|: the library's stated bound on its fp32 cosines
+SCORE_TOL = {"fp32": 1e-6, "bf16": 2e-6}   # |s_gpu - s_oracle| observed (below score_bound)
+SEL_REL_BAND = 1e-5       # the stated selection tolerance, relative to the boundary value
 ATTN_TOL = {"fp32": 1e-4, "bf16": 2e-2}    # max-abs on the attention output
+
+
+def score_bound(dtype: str, head_dim: int, group: int = 1, per_head: bool = False) -> float:
+    """The library's stated bound on |fp32 score - fp64 score| (cosine scores).
+
+    Rows rounded to fp32 (2 u; the per-head baseline's unit rows carry an
+    fp32 norm, d/2 + 3 u), the bf16 hi/lo split (2^-18), nt products summed
+    in fp32 (2 nt u), and the key norm, its square root and the quotient
+    ((d + 4) u), u = 2^-24."""
+    u = 2.0 ** -24
+    bf = dtype == "bf16"
+    gh = group if per_head else 1
+    nt = (2 if bf else 1) * head_dim * gh
+    rows = (head_dim / 2 + 3 if per_head else 2.0) * u
+    row = rows + (2.0 ** -18 * 1.01 if bf else 0.0) + 2 * nt * u * 1.01
+    return (row + (head_dim + 4) * u * 1.01) * 1.001
 
 
 def upload(w, device="cuda"):
@@ -66,8 +83,13 @@ def _band_check(got, want, values, boundary, band, what):
     return len(diff)
 
 
-def _rule_check(got, want, what):
-    assert np.array_equal(got, want), f"{what}: differs from the selection rule on its own values"
+def _rule_check(got, want, values, boundary, band, what):
+    """The GPU's set against the selection rule on its own fp32 values: equal except for
+    members within `band` of the GPU's fp32 boundary value (there it decided in fp64)."""
+    diff = set(got.tolist()) ^ set(want.tolist())
+    bad = [i for i in diff if abs(values[i] - boundary) > band]
+    assert not bad, (f"{what}: differs from the selection rule on its own values outside the "
+                     f"re-evaluation band ({len(bad)} members, first {bad[:5]})")
 
 
 def check_selection(w, r, heads=None, seqs=None):
@@ -95,11 +117,13 @@ def check_selection(w, r, heads=None, seqs=None):
             qi = r["q_idx"][s, h]
             assert np.all(qi[nq_eff:] == -1), f"{where}: q_idx padding"
             S_gpu = qi[:nq_eff].astype(np.int64)
-            _rule_check(S_gpu, oracle.lowest_cosine_queries(c_gpu, w.n_q), f"{where} q_idx")
             if c1 > c0:
+                _rule_check(S_gpu, oracle.lowest_cosine_queries(c_gpu, w.n_q), c_gpu,
+                            np.sort(c_gpu)[nq_eff - 1], 2 * QCOS_TOL, f"{where} q_idx")
                 S_or = oracle.lowest_cosine_queries(c_or, w.n_q)
                 bound = np.sort(c_or)[nq_eff - 1]
-                ties["q"] += _band_check(S_gpu, S_or, c_or, bound, QCOS_BAND, f"{where} q_idx")
+                ties["q"] += _band_check(S_gpu, S_or, c_or, bound, SEL_REL_BAND * abs(bound),
+                                         f"{where} q_idx")
             # stage 3: key scores, oracle on the GPU's kept queries
             s_gpu = r["scores"][h, h0:h1].astype(np.float64)
             s_or = oracle.key_scores(q_grp[S_gpu], kh[h0:h1, h])
@@ -110,12 +134,14 @@ def check_selection(w, r, heads=None, seqs=None):
             si = r["sel_idx"][s, h]
             assert np.all(si[b_eff:] == -1), f"{where}: sel_idx padding"
             I_gpu = si[:b_eff].astype(np.int64)
-            _rule_check(I_gpu, oracle.top_b_keys(s_gpu, w.budget), f"{where} sel_idx")
             if h1 > h0:
+                eps = score_bound(w.dtype, w.head_dim)
+                _rule_check(I_gpu, oracle.top_b_keys(s_gpu, w.budget), s_gpu,
+                            np.sort(s_gpu)[::-1][b_eff - 1], 2 * eps, f"{where} sel_idx")
                 I_or = oracle.top_b_keys(s_or, w.budget)
                 sb = np.sort(s_or)[::-1][b_eff - 1]
-                band = max(SEL_REL_BAND * abs(sb), 2 * SCORE_TOL[w.dtype])
-                ties["k"] += _band_check(I_gpu, I_or, s_or, sb, band, f"{where} sel_idx")
+                ties["k"] += _band_check(I_gpu, I_or, s_or, sb, SEL_REL_BAND * abs(sb),
+                                         f"{where} sel_idx")
     return ties
 
 
@@ -253,16 +279,15 @@ def check_variant_selection(w, r, variant):
                     assert np.array_equal(qi, r["q_idx"][s, 0]), f"{where}: subset not shared"
                     if c1 > c0:
                         bound = np.sort(cg_or)[nq_eff - 1]
-                        ties["q"] += _band_check(S_gpu, S_glob, cg_or, bound, QCOS_BAND,
-                                                 f"{where} q_idx")
-                else:
-                    _rule_check(S_gpu, oracle.lowest_cosine_queries(c_gpu, w.n_q),
-                                f"{where} q_idx")
-                    if c1 > c0:
-                        S_or = oracle.lowest_cosine_queries(c_or, w.n_q)
-                        bound = np.sort(c_or)[nq_eff - 1]
-                        ties["q"] += _band_check(S_gpu, S_or, c_or, bound, QCOS_BAND,
-                                                 f"{where} q_idx")
+                        ties["q"] += _band_check(S_gpu, S_glob, cg_or, bound,
+                                                 SEL_REL_BAND * abs(bound), f"{where} q_idx")
+                elif c1 > c0:
+                    _rule_check(S_gpu, oracle.lowest_cosine_queries(c_gpu, w.n_q), c_gpu,
+                                np.sort(c_gpu)[nq_eff - 1], 2 * QCOS_TOL, f"{where} q_idx")
+                    S_or = oracle.lowest_cosine_queries(c_or, w.n_q)
+                    bound = np.sort(c_or)[nq_eff - 1]
+                    ties["q"] += _band_check(S_gpu, S_or, c_or, bound, SEL_REL_BAND * abs(bound),
+                                             f"{where} q_idx")
             s_gpu = r["scores"][h, h0:h1].astype(np.float64)
             k_h = kh[h0:h1, h]
             tol = np.full(h1 - h0, SCORE_TOL[w.dtype])
@@ -282,10 +307,19 @@ def check_variant_selection(w, r, variant):
             si = r["sel_idx"][s, h]
             assert np.all(si[b_eff:] == -1), f"{where}: sel_idx padding"
             I_gpu = si[:b_eff].astype(np.int64)
-            _rule_check(I_gpu, oracle.top_b_keys(s_gpu, w.budget), f"{where} sel_idx")
             if h1 > h0:
+                rule = oracle.top_b_keys(s_gpu, w.budget)
                 I_or = oracle.top_b_keys(s_or, w.budget)
                 sb = np.sort(s_or)[::-1][b_eff - 1]
-                band = max(SEL_REL_BAND * abs(sb), 2 * float(np.max(tol)))
+                if variant == "dot":
+                    # unbounded dot products: no fp64 re-score, the fp32 rule decides, and
+                    # the oracle's set is matched within the scores' own error
+                    _rule_check(I_gpu, rule, s_gpu, 0.0, -1.0, f"{where} sel_idx")
+                    band = max(SEL_REL_BAND * abs(sb), 2 * float(np.max(tol)))
+                else:
+                    eps = score_bound(w.dtype, w.head_dim, G, per_head=variant == "per_head")
+                    _rule_check(I_gpu, rule, s_gpu, np.sort(s_gpu)[::-1][b_eff - 1], 2 * eps,
+                                f"{where} sel_idx")
+                    band = SEL_REL_BAND * abs(sb)
                 ties["k"] += _band_check(I_gpu, I_or, s_or, sb, band, f"{where} sel_idx")
     return ties

@@ -32,7 +32,7 @@ CASES = {
     "bf16_budget_above_data": ([(90, 50), (40, 500)], 8, 2, 128, "bf16", 200 // 2, 600, {}),
     "bf16_needles": ([(256, 3000), (128, 1500)], 8, 2, 128, "bf16", 8, 32,
                      dict(needles_per_head=4, outlier_needles=6.0)),
-    # decode-like chunks (C_s * G <= 8): the split-key attention kernel
+    # decode-like chunks (C_s * G <= 8): one partly filled 128-row attention tile per KV head
     "bf16_decode_g4": ([(1, 3000), (1, 0), (2, 500), (1, 64)], 8, 2, 128, "bf16", 1, 256, {}),
     "bf16_decode_g8": ([(1, 1500), (1, 70)], 16, 2, 128, "bf16", 2, 1000, dict(scaled=True)),
     "bf16_decode_d64_g1": ([(1, 2000), (1, 100), (1, 1)], 2, 2, 64, "bf16", 1, 300, {}),
@@ -105,7 +105,7 @@ def test_repeat_runs_are_bitwise_identical():
     shape, t = upload(w)
     ws = cpk.alloc_workspace(shape, w.n_q, w.budget)
     outs = []
-    for _ in range(5):
+    for _ in range(10):
         sel = torch.empty((w.num_seqs, w.num_kv_heads, w.budget), dtype=torch.int32,
                           device="cuda")
         o = cpk.prefill_chunk(shape, t["q"], t["k_hist"], t["v_hist"], t["k_chunk"],
@@ -188,8 +188,10 @@ ORDER_CASES = {
 
 @pytest.mark.parametrize("name", sorted(ORDER_CASES))
 def test_attention_tile_orders(name):
-    """The attention's workgroup orders (paired, wide, odd tile counts) against the oracle
-    on sampled rows, and the fused gather bit-identical to gather + attend."""
+    """The attention's workgroup orders (paired, wide, odd tile counts) against the oracle:
+    every row of the first and last KV head of the first and last sequence (all the
+    workgroups of those (sequence, KV head) pairs), sampled rows everywhere else; and the
+    fused gather bit-identical to gather + attend."""
     seqs, hq, hkv, d, dt, nq, b = ORDER_CASES[name]
     print(f"[gpu] attention order {name}", flush=True)
     w = make_case(seqs, hq, hkv, d, dt, nq, b, seed=31, name=name)
@@ -197,9 +199,12 @@ def test_attention_tile_orders(name):
     r = run_stages(w, shape, t)
     check_invariants(w, r)
     check_selection(w, r)
+    ends = sorted({0, w.num_seqs - 1})
+    full = check_attention(w, r, heads=sorted({0, hkv - 1}), seqs=ends)
     err = check_attention(w, r, rows=48, rng=np.random.default_rng(5))
     assert np.array_equal(r["out_fused"], r["out"])
-    print(f"[gpu] {name}: attention max-abs {err:.3g}", flush=True)
+    print(f"[gpu] {name}: attention max-abs {full:.3g} (all rows), {err:.3g} (sampled)",
+          flush=True)
 
 
 def test_cosines_skipped_when_every_token_is_kept():
