@@ -6,9 +6,9 @@ inputs already resident in HBM. By default the gather runs fused into the
 attention (quoka_select, then quoka_chunk_attn_gather); --unfused times the
 three separate calls (quoka_select, quoka_gather, quoka_chunk_attn); --variant
 times one of the pages' baseline selections in place of QUOKA's (then without
-the CPU baseline). Several rotated copies of the inputs are
-cycled through so that consecutive steps do not hit the 256 MB last-level
-cache with the previous step's history keys.
+the CPU baseline). Rotated copies of every input, at least 1 GiB of them in
+all, are cycled through, so a step finds none of its bytes in the 256 MB
+last-level cache.
 
 Prints ONE JSON line. `value` comes from a timed pass of the steps alone; a
 second timed pass brackets every stage with HIP events on the stream the
@@ -17,7 +17,7 @@ the first pass) and gives the stage times and the roofline entry for the
 dominant kernel (chunk attention, bf16 MFMA). cpu_baseline times the fp64
 oracle on a bounded sample of the same workload on the host cores.
 
-usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config llama8b]
+usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config long]
 """
 from __future__ import annotations
 
@@ -279,8 +279,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama8b", choices=sorted(DESCR))
-    ap.add_argument("--input-sets", type=int, default=4)
+    ap.add_argument("--config", default="long", choices=sorted(DESCR))
+    ap.add_argument("--input-sets", type=int, default=0,
+                    help="rotated copies of the inputs cycled through (default: enough for "
+                         "1 GiB, four times the 256 MB last-level cache, at least 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="gather into K/V_sel and attend in separate calls")
@@ -331,15 +333,19 @@ def main():
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     shape = cpk.Shape(w.cu_chunk, w.cu_hist, w.num_q_heads, w.num_kv_heads, w.head_dim,
                       w.dtype, device=dev)
-    base = {n: torch.from_numpy(getattr(w, n)).to(dt).to(dev)
-            for n in ("q", "k_hist", "v_hist", "k_chunk", "v_chunk")}
-    # rotated copies of the history (same work, different bytes) to defeat the LLC
+    names = ("q", "k_hist", "v_hist", "k_chunk", "v_chunk")
+    base = {n: torch.from_numpy(getattr(w, n)).to(dt).to(dev) for n in names}
+    # Rotated copies of every input (the same work on different bytes): a step
+    # finds nothing the previous steps left in the 256 MB last-level cache, so
+    # the bytes the kernels read come from HBM.
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    nsets = args.input_sets or min(16, max(2, -(-(1 << 30) // set_bytes)))
     sets = [base]
     TL = w.k_hist.shape[0]
-    for r in range(1, max(1, args.input_sets)):
-        shift = (r * TL) // args.input_sets
-        sets.append(dict(base, k_hist=torch.roll(base["k_hist"], shift, 0).contiguous(),
-                         v_hist=torch.roll(base["v_hist"], shift, 0).contiguous()))
+    TC = w.q.shape[0]
+    for r in range(1, nsets):
+        sets.append({n: torch.roll(base[n], (r * (TL if "hist" in n else TC)) // nsets, 0)
+                     .contiguous() for n in names})
     S, Hkv, B = w.num_seqs, w.num_kv_heads, w.budget
     ws = cpk.alloc_workspace(shape, w.n_q, B)
     sel = torch.empty((S, Hkv, B), dtype=torch.int32, device=dev)
@@ -349,25 +355,31 @@ def main():
         v_sel = torch.empty_like(k_sel)
     out = torch.empty_like(base["q"])
 
+    # ev (second pass): 0 before the selection, 1 before its scorer, 2 before its top-B,
+    # 3 after the selection, 4 after the gather, 5 after the attention
     def step(i, ev=None):
         x = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record()
-        cpk.select(shape, x["q"], x["k_hist"], w.n_q, B, sel_idx=sel, workspace=ws,
-                   variant=args.variant)
-        if ev is not None:
-            ev[1].record()
+        if ev is not None and args.variant == "quoka":
+            cpk.select_profiled(shape, x["q"], x["k_hist"], w.n_q, B, sel, ws, ev[0:4])
+        else:
+            if ev is not None:
+                ev[0].record()
+            cpk.select(shape, x["q"], x["k_hist"], w.n_q, B, sel_idx=sel, workspace=ws,
+                       variant=args.variant)
+            if ev is not None:
+                for e in ev[1:4]:
+                    e.record()
         if args.unfused:
             cpk.gather(shape, x["k_hist"], x["v_hist"], sel, B, k_sel=k_sel, v_sel=v_sel)
         if ev is not None:
-            ev[2].record()
+            ev[4].record()
         if args.unfused:
             cpk.chunk_attn(shape, x["q"], k_sel, v_sel, B, x["k_chunk"], x["v_chunk"], out=out)
         else:
             cpk.chunk_attn_gather(shape, x["q"], x["k_hist"], x["v_hist"], sel, B, x["k_chunk"],
                                   x["v_chunk"], out=out)
         if ev is not None:
-            ev[3].record()
+            ev[5].record()
 
     for i in range(args.warmup):
         step(i)
@@ -386,14 +398,16 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(args.warmup + args.steps + i, evs[i])
     torch.cuda.synchronize()
-    per = {"select": np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3,
-           "gather": np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3,
-           "attention": np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3}
+    span = lambda a, b: np.array([e[a].elapsed_time(e[b]) for e in evs]) * 1e3  # noqa: E731
+    per = {"select": span(0, 3), "gather": span(3, 4), "attention": span(4, 5)}
+    if args.variant == "quoka":
+        per.update({"select_query_side": span(0, 1), "select_scorer": span(1, 2),
+                    "select_topb": span(2, 3)})
     sel_us, gat_us, att_us = (float(np.mean(per[k])) for k in ("select", "gather", "attention"))
     pct = {k: {"p10": round(float(np.percentile(v, 10)), 2),
                "p50": round(float(np.percentile(v, 50)), 2),
@@ -440,9 +454,16 @@ def main():
         "secondary": ({"gather_GBps": gbytes / (gat_us * 1e-6) / 1e9,
                        "gather_frac_hbm": gbytes / (gat_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                        "gather_bytes": gbytes} if args.unfused else
-                      {"gather": "fused into the attention (quoka_chunk_attn_gather)"}) |
-                     {"scorer_bytes": scorer_bytes(w)},
+                      {"gather": "fused into the attention (quoka_chunk_attn_gather)"}),
     }
+    if args.variant == "quoka":
+        sc_us = float(np.mean(per["select_scorer"]))
+        sc_gbs = scorer_bytes(w) / (sc_us * 1e-6) / 1e9
+        line["secondary"].update({
+            "scorer_us": round(sc_us, 2), "scorer_bytes": scorer_bytes(w),
+            "scorer_GBps": round(sc_gbs, 1), "scorer_frac_hbm": round(sc_gbs / PEAK_HBM_GBS, 4),
+            "scorer_timing": "HIP events around the scorer launch, same run (the launch gap "
+                             "included)"})
     if not args.no_cpu_baseline and args.variant == "quoka":
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -27,9 +27,11 @@ MAX_Q_BUDGET = 128
 VARIANTS = {"quoka": 0, "dot": 1, "mean_queries": 2, "mean_query": 3, "per_head": 4,
             "global": 5}
 
-SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_select_variant", "quoka_gather",
+SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
+           "quoka_select_variant", "quoka_gather",
            "quoka_chunk_attn",
-           "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prompt_workspace_bytes",
+           "quoka_chunk_attn_gather", "quoka_prefill_chunk",
+           "quoka_prompt_workspace_bytes",
            "quoka_prefill_prompt", "quoka_strerror", "quoka_last_error")
 
 
@@ -83,6 +85,7 @@ def load_library(path: str = LIB_PATH):
     lib.quoka_workspace_bytes.argtypes = [sp, i32, i32, P(sz)]
     lib.quoka_select.argtypes = [sp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.quoka_select_variant.argtypes = [sp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.quoka_select_profiled.argtypes = [sp, vp, vp, i32, i32, vp, vp, sz, vp, vp]
     lib.quoka_gather.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp]
     lib.quoka_chunk_attn.argtypes = [sp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp]
     lib.quoka_chunk_attn_gather.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
@@ -93,9 +96,10 @@ def load_library(path: str = LIB_PATH):
     lib.quoka_prompt_workspace_bytes.argtypes = [pp, i32, i32, P(sz)]
     lib.quoka_prefill_prompt.argtypes = [pp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp,
                                          sz, vp]
-    for f in ("quoka_workspace_bytes", "quoka_select", "quoka_gather", "quoka_chunk_attn",
-              "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prompt_workspace_bytes",
-              "quoka_prefill_prompt"):
+    for f in ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
+              "quoka_select_variant", "quoka_gather", "quoka_chunk_attn",
+              "quoka_chunk_attn_gather", "quoka_prefill_chunk",
+              "quoka_prompt_workspace_bytes", "quoka_prefill_prompt"):
         getattr(lib, f).restype = ctypes.c_int
     lib.quoka_strerror.argtypes = [ctypes.c_int]
     lib.quoka_strerror.restype = ctypes.c_char_p
@@ -228,6 +232,28 @@ def select(shape: Shape, q, k_hist, q_budget: int, kv_budget: int, *, sel_idx=No
                                         workspace.numel(), _stream(dev)),
                "quoka_select_variant")
     return {"sel_idx": sel_idx, "q_idx": q_idx, "qcos": qcos, "scores": scores}
+
+
+def select_profiled(shape: Shape, q, k_hist, q_budget: int, kv_budget: int, sel_idx, workspace,
+                    events):
+    """quoka_select with four torch.cuda.Event (enable_timing) recorded between its stages:
+    before the query side, before the scorer, before the top-B launches and after them."""
+    lib = load_library()
+    S, Hq, Hkv, d = shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    shape._check_tensor(q, "q", (shape.total_chunk, Hq, d), shape.torch_dtype)
+    shape._check_tensor(k_hist, "k_hist", (shape.total_hist, Hkv, d), shape.torch_dtype)
+    shape._check_tensor(sel_idx, "sel_idx", (S, Hkv, kv_budget), torch.int32)
+    if len(events) != 4:
+        raise ValueError("four events are needed")
+    for e in events:  # torch creates the HIP event on its first record
+        if not e.cuda_event:
+            e.record()
+    handles = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    _check(lib.quoka_select_profiled(ctypes.byref(shape.c), _ptr(q), _ptr(k_hist), q_budget,
+                                     kv_budget, _ptr(sel_idx), _ptr(workspace),
+                                     workspace.numel(), handles, _stream(shape.device)),
+           "quoka_select_profiled")
+    return sel_idx
 
 
 def gather(shape: Shape, k_hist, v_hist, sel_idx, kv_budget: int, *, k_sel=None, v_sel=None):

@@ -221,7 +221,6 @@ Workspace workspace_layout(const Problem& p) {
   w.zero_end = o;
   w.thr = take(SH * sizeof(Threshold));
   w.cand = take((size_t)p.Hkv * p.TL * 8);
-  w.cand2 = take((size_t)p.Hkv * p.TL * 8);
   w.ctcount = take((size_t)p.Hkv * p.NKT * 4);
   w.qkey = take((size_t)p.Hkv * p.TC * 8);
   w.row0 = take(SH * p.D * 8);
@@ -238,18 +237,28 @@ using namespace quoka;
 
 namespace {
 
+// events, when given: four events recorded before the query side, after it,
+// after the scorer and after the top-B launches.
 quoka_status run_select(const Problem& p, const Workspace& w, const void* q, const void* k_hist,
                         int32_t* sel_idx, int32_t* q_idx_opt, float* qcos_opt, float* scores_opt,
-                        char* ws, hipStream_t st) {
+                        char* ws, hipStream_t st, hipEvent_t* events = nullptr) {
   quoka_status rc = ensure_lds(p);
   if (rc != QUOKA_OK) return rc;
   float* qcos = qcos_opt ? qcos_opt : (float*)(ws + w.qcos);
   float* scores = scores_opt ? scores_opt : (float*)(ws + w.scores);
   int32_t* qidx = q_idx_opt ? q_idx_opt : (int32_t*)(ws + w.qidx);
+  auto mark = [&](int i) -> quoka_status {
+    return events ? hip_check(hipEventRecord(events[i], st), "hipEventRecord", st) : QUOKA_OK;
+  };
+  if ((rc = mark(0))) return rc;
   if ((rc = hip_check(launch_qprep(p, q, ws, w, qcos, qcos_opt != nullptr, qidx, sel_idx, st), "qprep", st)))
     return rc;
+  if ((rc = mark(1))) return rc;
   if ((rc = hip_check(launch_scorer(p, k_hist, ws, w, scores, st), "scorer", st))) return rc;
-  return hip_check(launch_topb(p, q, k_hist, qidx, ws, w, scores, sel_idx, st), "topb", st);
+  if ((rc = mark(2))) return rc;
+  if ((rc = hip_check(launch_topb(p, q, k_hist, qidx, ws, w, scores, sel_idx, st), "topb", st)))
+    return rc;
+  return mark(3);
 }
 
 #define QUOKA_NEED(ptr, total)                                                          \
@@ -291,6 +300,29 @@ quoka_status quoka_select(const quoka_shape* shape, const void* q, const void* k
     return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   return run_select(p, w, q, k_hist, sel_idx, q_idx_opt, qcos_opt, scores_opt, (char*)ws,
                     stream);
+}
+
+quoka_status quoka_select_profiled(const quoka_shape* shape, const void* q, const void* k_hist,
+                                   int32_t q_budget, int32_t kv_budget, int32_t* sel_idx,
+                                   void* ws, size_t ws_bytes, hipEvent_t* events,
+                                   hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, q_budget, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(q, p.TC);
+  QUOKA_NEED(k_hist, p.TL);
+  QUOKA_NEED(sel_idx, 1);
+  if (!events) return fail(QUOKA_EINVAL, "events is null");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(QUOKA_EINVAL, "events[%d] is null", i);
+  if (!ws) return fail(QUOKA_EWORKSPACE, "workspace is null");
+  if (!aligned16(ws)) return fail(QUOKA_EINVAL, "workspace is not 16-byte aligned");
+  const Workspace w = workspace_layout(p);
+  if (ws_bytes < w.total)
+    return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  return run_select(p, w, q, k_hist, sel_idx, nullptr, nullptr, nullptr, (char*)ws, stream,
+                    events);
 }
 
 quoka_status quoka_select_variant(const quoka_shape* shape, int32_t variant, const void* q,

@@ -66,7 +66,6 @@ struct Workspace {
   size_t thr;       // Threshold [S, Hkv]
   size_t ctcount;   // uint32 [Hkv, NKT] candidates per tile
   size_t cand;      // uint64 [Hkv, TL] candidates, each tile's in its own key range
-  size_t cand2;     // uint64 [Hkv, TL] a problem's candidates gathered (beyond the LDS)
   size_t gtcount;   // uint32 [Hkv, NKT] keys above the threshold bin per tile
   size_t chcount;   // uint32 [Hkv, NKT] chosen candidates per tile
   size_t bits;      // uint32 bitmap over [Hkv, TL]: chosen candidates

@@ -76,7 +76,6 @@ struct TopbArgs {
   const uint32_t* hist;
   Threshold* thr;
   uint64_t* cand;          // [Hkv, TL]: tile t's candidates at its own keys' offsets
-  uint64_t* cand2;         // [Hkv, TL]: a problem's candidates gathered, past the LDS
   uint32_t* ctcount;       // [Hkv, NKT] candidates per tile
   uint32_t* gtcount;
   uint32_t* chcount;
@@ -459,10 +458,14 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(const TopbArgs a) {
   uint32_t n = 0u;
   for (int i = threadIdx.x; i < ntile; i += 256) n += ctc[i];
   n = block_sum<256>(n, rs);
-  uint64_t* dst = n <= (uint32_t)kCandCap ? lc : a.cand2 + (int64_t)h * a.TL + h_off;
-  // gathered 256 tiles at a time: their offsets by a scan, then every thread
+  // Gathered 256 tiles at a time: their offsets by a scan, then every thread
   // copies entries (finding each one's tile by a binary search over the
-  // offsets), so that the loads are all in flight together
+  // offsets), so that the loads are all in flight together. Past the LDS the
+  // candidates are compacted in place to the front of the problem's list:
+  // entry i comes from position >= i, so 256 entries at a time are read into
+  // registers and written after a barrier.
+  const bool in_lds = n <= (uint32_t)kCandCap;
+  uint64_t* dst = in_lds ? lc : a.cand + (int64_t)h * a.TL + h_off;
   __shared__ uint32_t toff[257];
   uint32_t base = 0u;
   for (int t0 = 0; t0 < ntile; t0 += 256) {
@@ -473,13 +476,20 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(const TopbArgs a) {
     if (threadIdx.x == 255) toff[256] = excl + c;
     __syncthreads();
     const uint32_t m = toff[256];
-    for (uint32_t i = threadIdx.x; i < m; i += 256) {
-      int lo = 0, hi = nt - 1;  // last tile whose offset is <= i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (toff[mid] <= i) lo = mid; else hi = mid - 1;
+    for (uint32_t i0 = 0; i0 < m; i0 += 256) {
+      const uint32_t i = i0 + threadIdx.x;
+      uint64_t v = 0ull;
+      if (i < m) {
+        int lo = 0, hi = nt - 1;  // last tile whose offset is <= i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (toff[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        v = crow[(int64_t)(t0 + lo) * kTopbKeys + (i - toff[lo])];
       }
-      dst[base + i] = crow[(int64_t)(t0 + lo) * kTopbKeys + (i - toff[lo])];
+      if (!in_lds) __syncthreads();
+      if (i < m) dst[base + i] = v;
+      if (!in_lds) __syncthreads();
     }
     base += m;
     __syncthreads();
@@ -594,7 +604,6 @@ hipError_t launch_topb(const Problem& p, const void* q, const void* k_hist, cons
   a.hist = (const uint32_t*)(ws + w.hist);
   a.thr = (Threshold*)(ws + w.thr);
   a.cand = (uint64_t*)(ws + w.cand);
-  a.cand2 = (uint64_t*)(ws + w.cand2);
   a.ctcount = (uint32_t*)(ws + w.ctcount);
   a.gtcount = (uint32_t*)(ws + w.gtcount);
   a.chcount = (uint32_t*)(ws + w.chcount);

@@ -119,6 +119,18 @@ quoka_status quoka_select(const quoka_shape* shape, const void* q,
                           float* scores_opt, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* quoka_select (no optional outputs) with four caller-created HIP events
+ * recorded on `stream`: events[0] before the query side (pre-aggregation,
+ * cosines, subselection), events[1] before the key scorer, events[2] before
+ * the top-B launches, events[3] after them. For measuring the stages of the
+ * selection; the selection itself is the same. QUOKA_EINVAL if events or one
+ * of its four entries is null. */
+quoka_status quoka_select_profiled(const quoka_shape* shape, const void* q,
+                                   const void* k_hist, int32_t q_budget,
+                                   int32_t kv_budget, int32_t* sel_idx, void* ws,
+                                   size_t ws_bytes, hipEvent_t* events,
+                                   hipStream_t stream);
+
 /* Baseline selections the pages set QUOKA against, for speed and parity
  * comparisons (the pages' accuracy claims for them need benchmark data).
  * Each replaces one step of the selection; everything else is as in
