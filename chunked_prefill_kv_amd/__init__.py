@@ -30,7 +30,7 @@ VARIANTS = {"quoka": 0, "dot": 1, "mean_queries": 2, "mean_query": 3, "per_head"
 SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
            "quoka_select_variant", "quoka_gather",
            "quoka_chunk_attn",
-           "quoka_chunk_attn_gather", "quoka_prefill_chunk",
+           "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prefill_chunk_static",
            "quoka_prompt_workspace_bytes",
            "quoka_prefill_prompt", "quoka_strerror", "quoka_last_error")
 
@@ -92,13 +92,15 @@ def load_library(path: str = LIB_PATH):
                                             vp]
     lib.quoka_prefill_chunk.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
                                         vp, vp, sz, vp]
+    lib.quoka_prefill_chunk_static.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32,
+                                               ctypes.c_float, vp, vp, vp]
     pp = ctypes.POINTER(_CPrompt)
     lib.quoka_prompt_workspace_bytes.argtypes = [pp, i32, i32, P(sz)]
     lib.quoka_prefill_prompt.argtypes = [pp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp,
                                          sz, vp]
     for f in ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
               "quoka_select_variant", "quoka_gather", "quoka_chunk_attn",
-              "quoka_chunk_attn_gather", "quoka_prefill_chunk",
+              "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prefill_chunk_static",
               "quoka_prompt_workspace_bytes", "quoka_prefill_prompt"):
         getattr(lib, f).restype = ctypes.c_int
     lib.quoka_strerror.argtypes = [ctypes.c_int]

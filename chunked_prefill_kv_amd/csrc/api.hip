@@ -267,6 +267,30 @@ quoka_status run_select(const Problem& p, const Workspace& w, const void* q, con
     if ((ptr) && !aligned16(ptr)) return fail(QUOKA_EINVAL, "%s is not 16-byte aligned", #ptr); \
   } while (0)
 
+// Scratch of quoka_prefill_chunk_static: one array per device the library
+// runs on, held until the process ends. Host code never uses its name as an
+// address: the device address comes from hipGetSymbolAddress, per device.
+constexpr size_t kStaticScratchBytes = (size_t)QUOKA_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+
+quoka_status static_scratch(char** out) {
+  static std::mutex mu;
+  static char* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QUOKA_EHIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(QUOKA_EUNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(QUOKA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    addr[dev] = (char*)ptr;
+  }
+  *out = addr[dev];
+  return QUOKA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -428,6 +452,40 @@ quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q, const 
   if (ws_bytes < w.total)
     return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   char* base = (char*)ws;
+  int32_t* sel = sel_idx_opt ? sel_idx_opt : (int32_t*)(base + w.selidx);
+  rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
+  if (rc != QUOKA_OK) return rc;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
+  return hip_check(
+      launch_attention(p, q, k_hist, v_hist, sel, k_chunk, v_chunk, scale, out, stream),
+      "attention", stream);
+}
+
+quoka_status quoka_prefill_chunk_static(const quoka_shape* shape, const void* q,
+                                        const void* k_hist, const void* v_hist,
+                                        const void* k_chunk, const void* v_chunk,
+                                        int32_t q_budget, int32_t kv_budget,
+                                        float softmax_scale, void* out, int32_t* sel_idx_opt,
+                                        hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, q_budget, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(q, p.TC);
+  QUOKA_NEED(k_hist, p.TL);
+  QUOKA_NEED(v_hist, p.TL);
+  QUOKA_NEED(k_chunk, p.TC);
+  QUOKA_NEED(v_chunk, p.TC);
+  QUOKA_NEED(out, p.TC);
+  if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
+  const Workspace w = workspace_layout(p);
+  if (w.total > kStaticScratchBytes)
+    return fail(QUOKA_EUNSUPPORTED,
+                "this problem needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use quoka_prefill_chunk with a workspace)",
+                w.total, kStaticScratchBytes);
+  char* base = nullptr;
+  if ((rc = static_scratch(&base))) return rc;
   int32_t* sel = sel_idx_opt ? sel_idx_opt : (int32_t*)(base + w.selidx);
   rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
   if (rc != QUOKA_OK) return rc;

@@ -221,6 +221,26 @@ quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q,
                                  int32_t* sel_idx_opt, void* ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the device scratch quoka_prefill_chunk_static works in. */
+#define QUOKA_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* quoka_prefill_chunk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with its scratch in a static
+ * device array of QUOKA_STATIC_SCRATCH_BYTES held by the library for each
+ * device it runs on until the process ends (its device address is looked up
+ * on the first call on a device). It allocates and frees nothing. The caller
+ * still passes every input and output. Problems whose workspace
+ * (quoka_workspace_bytes) exceeds that size return QUOKA_EUNSUPPORTED. Every
+ * call on a device shares that device's array: calls that overlap on one
+ * device (other streams or threads) race and must be ordered by the caller. */
+quoka_status quoka_prefill_chunk_static(const quoka_shape* shape, const void* q,
+                                        const void* k_hist, const void* v_hist,
+                                        const void* k_chunk, const void* v_chunk,
+                                        int32_t q_budget, int32_t kv_budget,
+                                        float softmax_scale, void* out,
+                                        int32_t* sel_idx_opt, hipStream_t stream);
+
 /* A whole prompt of one sequence, processed by chunked prefill. */
 typedef struct quoka_prompt {
   int32_t num_q_heads;            /* H_q */
