@@ -399,6 +399,18 @@ def pin_variant_global_with_one_kv_head_is_quoka():
     np.testing.assert_allclose(a["s"], b["s"], atol=1e-15)
 
 
+def pin_effective_budgets_match_the_selections():
+    # the clamp the checks use equals the sizes select_for_head actually returns (its
+    # sorts slice to min(n_q, C) and min(B, L)), over budgets below, at and above the data
+    rng = np.random.default_rng(11)
+    for C, L in ((5, 9), (1, 1), (7, 0), (3, 40), (12, 12)):
+        q = rng.standard_normal((C, 2, 4))
+        k = rng.standard_normal((L, 4))
+        for nq, b in ((1, 1), (4, 8), (C, L if L else 1), (C + 3, L + 5), (50, 2)):
+            r = oracle.select_for_head(q, k, nq, b)
+            assert oracle.effective_budgets(C, L, nq, b) == (r["S"].shape[0], r["I"].shape[0])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -466,6 +478,7 @@ def _mutations():
         "mask_without_diagonal": ("attend_rows", causal_strict),
         "chunk_mask_without_diagonal": ("attend_chunk", chunk_strict),
         "global_from_first_head_only": ("global_query_cosines", global_head0),
+        "budgets_not_clamped": ("effective_budgets", lambda C, L, nq, b: (int(nq), int(b))),
     }
 
 
