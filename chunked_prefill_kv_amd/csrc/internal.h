@@ -78,10 +78,8 @@ struct Workspace {
 
 struct Threshold {
   int32_t bstar;           // bin holding the B_eff-th score; -1 = keep everything
-  int32_t above;           // keys in bins above bin_hi (all kept)
-  int32_t need;            // keys to choose among the candidates
-  int32_t bin_lo, bin_hi;  // candidate window of bins around bstar
-  int32_t pad[3];
+  int32_t pad;
+  double lo, hi;           // candidates: scores in [lo, hi]; above hi kept, below lo not
 };
 
 // |fp32 cosine to the mean query - fp64 cosine|. The stored g is the fp64

@@ -14,16 +14,17 @@
 //
 // Three launches:
 //   filter : every workgroup derives from the scorer's histogram the bin b*
-//            holding s_B and a window of bins [b* - W, b* + W] that contains
-//            every key within 2 eps of any score in b*; keys above the window
-//            are in; the keys of its tile inside the window are scored in
-//            fp64 and stored, as unique keys (fp64 value, then lower index
-//            first), at the tile's own offset of the candidate list;
+//            holding s_B; the candidate window [lo, hi] is b*'s score range
+//            widened by 2 eps on each side, so it holds every key within
+//            2 eps of s_B; keys above hi are in and counted per tile; the keys
+//            of its tile inside the window are scored in fp64 and stored, as
+//            unique keys (fp64 value, then lower index first), at the tile's
+//            own offset of the candidate list;
 //   cands  : one workgroup per problem: the tiles' candidates gathered, radix
-//            select of the `need` best; the chosen ones are marked in a bitmap
-//            and counted per tile;
+//            select of the B_eff - (keys above hi) best; the chosen ones are
+//            marked in a bitmap and counted per tile;
 //   write  : each tile offsets itself by the counts of the tiles before it and
-//            writes its kept indices (above the window, or marked) ascending.
+//            writes its kept indices (above hi, or marked) ascending.
 // The dot-product baseline's scores carry no such bound (they are not
 // normalised): its window is the single bin b* and its candidates keep their
 // fp32 scores.
@@ -71,7 +72,8 @@ struct TopbArgs {
   const int32_t* plan;
   int S, Hq, Hkv, G;
   int64_t TL, NKT;
-  int kv_budget, window;
+  int kv_budget;
+  double eps;              // |fp32 score - fp64 score| <= eps
   const float* scores;
   const uint32_t* hist;
   Threshold* thr;
@@ -384,23 +386,34 @@ __global__ __launch_bounds__(256, 2) void topb_filter_kernel(const TopbArgs a) {
   const uint32_t* hp = a.hist + (int64_t)prob * kScoreBins;
   const int b_eff = min(a.kv_budget, L);
   Threshold t;
-  find_threshold_bin<256>(hp, L, b_eff, rs, &t.bstar, &t.above, &t.need);
-  t.bin_lo = t.bin_hi = t.bstar;
-  if (t.bstar >= 0) {
-    t.bin_lo = max(0, t.bstar - a.window);
-    t.bin_hi = min(kScoreBins - 1, t.bstar + a.window);
-    for (int b = t.bstar + 1; b <= t.bin_hi; ++b) t.above -= (int)hp[b];
-    t.need = b_eff - t.above;
+  {
+    int above, need;
+    find_threshold_bin<256>(hp, L, b_eff, rs, &t.bstar, &above, &need);
   }
+  t.pad = 0;
+  // the window: kRaw, the bin b* itself; else b*'s score range (a score s
+  // lands in bin floor(fp32(s + 1) * 1024), fp32(s + 1) within 2^-23 of
+  // s + 1) widened by 2 eps on each side
+  t.lo = (double)t.bstar / (kScoreBins / 2) - 1.0 - 0x1p-22 - 2.0 * a.eps;
+  t.hi = (double)(t.bstar + 1) / (kScoreBins / 2) - 1.0 + 0x1p-22 + 2.0 * a.eps;
   uint32_t gt = 0, nc = 0;
   uint64_t bal[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int key = k0 + i * 256 + threadIdx.x;
-    const bool ok = key < L;
-    const int bin = bin_of<kRaw>(sc[i]);
-    gt += (ok && bin > t.bin_hi);
-    bal[i] = __ballot(ok && bin >= t.bin_lo && bin <= t.bin_hi);
+    const bool ok = key < L && t.bstar >= 0;
+    bool above, cand;
+    if constexpr (kRaw) {
+      const int bin = bin_of<true>(sc[i]);
+      above = bin > t.bstar;
+      cand = bin == t.bstar;
+    } else {
+      const double v = (double)sc[i];
+      above = v > t.hi;
+      cand = v >= t.lo && !above;
+    }
+    gt += (ok && above);
+    bal[i] = __ballot(ok && cand);
     nc += (uint32_t)__popcll(bal[i]);
   }
   if (lane == 0) wcnt[wave] = nc;
@@ -454,10 +467,16 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(const TopbArgs a) {
   if (t.bstar < 0) return;  // every key is kept
   const int ntile = kt_off[s + 1] - kt_off[s];
   const uint32_t* ctc = a.ctcount + (int64_t)h * a.NKT + kt_off[s];
+  const uint32_t* gtc = a.gtcount + (int64_t)h * a.NKT + kt_off[s];
   const uint64_t* crow = a.cand + (int64_t)h * a.TL + h_off;
-  uint32_t n = 0u;
-  for (int i = threadIdx.x; i < ntile; i += 256) n += ctc[i];
+  uint32_t n = 0u, above = 0u;
+  for (int i = threadIdx.x; i < ntile; i += 256) {
+    n += ctc[i];
+    above += gtc[i];
+  }
   n = block_sum<256>(n, rs);
+  above = block_sum<256>(above, rs);
+  const int need = min(a.kv_budget, L) - (int)above;  // 1 <= need <= n
   // Gathered 256 tiles at a time: their offsets by a scan, then every thread
   // copies entries (finding each one's tile by a binary search over the
   // offsets), so that the loads are all in flight together. Past the LDS the
@@ -495,8 +514,8 @@ __global__ __launch_bounds__(256) void topb_cands_kernel(const TopbArgs a) {
     __syncthreads();
   }
   uint64_t prefix = 0ull, mask = 0ull;  // n == need: every candidate is chosen
-  if (t.need < (int)n)
-    radix_select<true, 256>([&](int i) { return dst[i]; }, (int)n, t.need, rs, prefix, mask);
+  if (need < (int)n)
+    radix_select<true, 256>([&](int i) { return dst[i]; }, (int)n, need, rs, prefix, mask);
   auto index_of = [](uint64_t c) { return kRaw ? cand_index(c) : exact_key_index_desc(c); };
 
   // Chosen candidates per tile, counted in LDS (this workgroup owns every
@@ -561,8 +580,17 @@ __global__ __launch_bounds__(256) void topb_write_kernel(const TopbArgs a, int32
   for (int e = 0; e < PER; ++e) {
     const int key = k0 + e;
     if (key < L) {
-      const int bin = bin_of<kRaw>(scv[e]);
-      const bool sel = t.bstar < 0 || bin > t.bin_hi || (bin >= t.bin_lo && (mine >> e & 1u));
+      bool above, cand;
+      if constexpr (kRaw) {
+        const int bin = bin_of<true>(scv[e]);
+        above = bin > t.bstar;
+        cand = bin == t.bstar;
+      } else {
+        const double v = (double)scv[e];
+        above = v > t.hi;
+        cand = v >= t.lo;
+      }
+      const bool sel = t.bstar < 0 || above || (cand && (mine >> e & 1u));
       flags |= (uint32_t)sel << e;
       cnt += sel;
     }
@@ -573,13 +601,6 @@ __global__ __launch_bounds__(256) void topb_write_kernel(const TopbArgs a, int32
 #pragma unroll
   for (int e = 0; e < PER; ++e)
     if ((flags & (1u << e)) && pos < b_eff) out[pos++] = k0 + e;
-}
-
-// Half-width in bins of the candidate window: every key within 2 eps of a
-// score of bin b* lies in the bins [b* - W, b* + W] (a score's bin is taken
-// from fp32(s + 1) * 1024, which may move s by 2^-23).
-int topb_window(float eps) {
-  return (int)std::floor((2.0 * eps + 0x1p-22) * (kScoreBins / 2)) + 1;
 }
 
 hipError_t launch_topb(const Problem& p, const void* q, const void* k_hist, const int32_t* qidx,
@@ -599,7 +620,7 @@ hipError_t launch_topb(const Problem& p, const void* q, const void* k_hist, cons
   a.TL = p.TL;
   a.NKT = p.NKT;
   a.kv_budget = p.kv_budget;
-  a.window = raw ? 0 : topb_window(eb.eps);
+  a.eps = eb.eps;
   a.scores = scores;
   a.hist = (const uint32_t*)(ws + w.hist);
   a.thr = (Threshold*)(ws + w.thr);
