@@ -241,11 +241,14 @@ def bench_prompt(args):
             idx.fill_(-1)
         idx = idx.view(1, 1, kb).expand(1, Hkv, kb).contiguous()
         dense_calls.append((shape, a, b, kb, idx))
+    # the attention's own workspace (key-range states of short chunks), allocated once
+    dense_ws = torch.empty(max([cpk.attn_workspace_bytes(c[0], c[3]) for c in dense_calls] + [16]),
+                           dtype=torch.uint8, device="cuda")
 
     def dense():
         for shape, a, b, kb, idx in dense_calls:
             cpk.chunk_attn_gather(shape, q[a:b], k[:a], v[:a], idx, kb, k[a:b], v[a:b],
-                                  out=out[a:b])
+                                  out=out[a:b], workspace=dense_ws)
 
     res = {}
     for name, fn in (("quoka", quoka), ("dense", dense)):
@@ -374,10 +377,11 @@ def main():
         if ev is not None:
             ev[4].record()
         if args.unfused:
-            cpk.chunk_attn(shape, x["q"], k_sel, v_sel, B, x["k_chunk"], x["v_chunk"], out=out)
+            cpk.chunk_attn(shape, x["q"], k_sel, v_sel, B, x["k_chunk"], x["v_chunk"], out=out,
+                           workspace=ws)
         else:
             cpk.chunk_attn_gather(shape, x["q"], x["k_hist"], x["v_hist"], sel, B, x["k_chunk"],
-                                  x["v_chunk"], out=out)
+                                  x["v_chunk"], out=out, workspace=ws)
         if ev is not None:
             ev[5].record()
 

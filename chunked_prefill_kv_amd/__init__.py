@@ -29,7 +29,7 @@ VARIANTS = {"quoka": 0, "dot": 1, "mean_queries": 2, "mean_query": 3, "per_head"
 
 SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
            "quoka_select_variant", "quoka_gather",
-           "quoka_chunk_attn",
+           "quoka_attn_workspace_bytes", "quoka_chunk_attn",
            "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prefill_chunk_static",
            "quoka_prompt_workspace_bytes",
            "quoka_prefill_prompt", "quoka_strerror", "quoka_last_error")
@@ -87,9 +87,10 @@ def load_library(path: str = LIB_PATH):
     lib.quoka_select_variant.argtypes = [sp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.quoka_select_profiled.argtypes = [sp, vp, vp, i32, i32, vp, vp, sz, vp, vp]
     lib.quoka_gather.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp]
-    lib.quoka_chunk_attn.argtypes = [sp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp]
+    lib.quoka_attn_workspace_bytes.argtypes = [sp, i32, P(sz)]
+    lib.quoka_chunk_attn.argtypes = [sp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.quoka_chunk_attn_gather.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
-                                            vp]
+                                            vp, sz, vp]
     lib.quoka_prefill_chunk.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp,
                                         vp, vp, sz, vp]
     lib.quoka_prefill_chunk_static.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32,
@@ -193,6 +194,26 @@ def workspace_bytes(shape: Shape, q_budget: int, kv_budget: int) -> int:
     return int(n.value)
 
 
+def attn_workspace_bytes(shape: Shape, kv_budget: int) -> int:
+    """Workspace bytes chunk_attn / chunk_attn_gather need (0 for most shapes)."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.quoka_attn_workspace_bytes(ctypes.byref(shape.c), kv_budget, ctypes.byref(n)),
+           "quoka_attn_workspace_bytes")
+    return int(n.value)
+
+
+def _attn_workspace(shape: Shape, kv_budget: int, workspace):
+    if workspace is None:
+        n = attn_workspace_bytes(shape, kv_budget)
+        workspace = torch.empty(n, dtype=torch.uint8, device=shape.device) if n else None
+    if workspace is None:
+        return None, 0
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    return workspace, workspace.numel()
+
+
 def alloc_workspace(shape: Shape, q_budget: int, kv_budget: int) -> torch.Tensor:
     return torch.empty(workspace_bytes(shape, q_budget, kv_budget), dtype=torch.uint8,
                        device=shape.device)
@@ -275,7 +296,7 @@ def gather(shape: Shape, k_hist, v_hist, sel_idx, kv_budget: int, *, k_sel=None,
 
 
 def chunk_attn(shape: Shape, q, k_sel, v_sel, kv_budget: int, k_chunk, v_chunk,
-               softmax_scale: float = 0.0, *, out=None):
+               softmax_scale: float = 0.0, *, out=None, workspace=None):
     lib = load_library()
     S, Hq, Hkv, d = shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
     shape._check_tensor(q, "q", (shape.total_chunk, Hq, d), shape.torch_dtype)
@@ -286,14 +307,16 @@ def chunk_attn(shape: Shape, q, k_sel, v_sel, kv_budget: int, k_chunk, v_chunk,
     if out is None:
         out = torch.empty_like(q)
     shape._check_tensor(out, "out", tuple(q.shape), shape.torch_dtype)
+    ws, nws = _attn_workspace(shape, kv_budget, workspace)
     _check(lib.quoka_chunk_attn(ctypes.byref(shape.c), _ptr(q), _ptr(k_sel), _ptr(v_sel),
                                 kv_budget, _ptr(k_chunk), _ptr(v_chunk), float(softmax_scale),
-                                _ptr(out), _stream(shape.device)), "quoka_chunk_attn")
+                                _ptr(out), _ptr(ws), nws, _stream(shape.device)),
+           "quoka_chunk_attn")
     return out
 
 
 def chunk_attn_gather(shape: Shape, q, k_hist, v_hist, sel_idx, kv_budget: int, k_chunk,
-                      v_chunk, softmax_scale: float = 0.0, *, out=None):
+                      v_chunk, softmax_scale: float = 0.0, *, out=None, workspace=None):
     """Gather fused into the chunk attention: equals gather() then chunk_attn()."""
     lib = load_library()
     S, Hq, Hkv, d = shape.num_seqs, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
@@ -306,10 +329,11 @@ def chunk_attn_gather(shape: Shape, q, k_hist, v_hist, sel_idx, kv_budget: int, 
     if out is None:
         out = torch.empty_like(q)
     shape._check_tensor(out, "out", tuple(q.shape), shape.torch_dtype)
+    ws, nws = _attn_workspace(shape, kv_budget, workspace)
     _check(lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), _ptr(q), _ptr(k_hist),
                                        _ptr(v_hist), _ptr(sel_idx), kv_budget, _ptr(k_chunk),
-                                       _ptr(v_chunk), float(softmax_scale), _ptr(out),
-                                       _stream(shape.device)), "quoka_chunk_attn_gather")
+                                       _ptr(v_chunk), float(softmax_scale), _ptr(out), _ptr(ws),
+                                       nws, _stream(shape.device)), "quoka_chunk_attn_gather")
     return out
 
 

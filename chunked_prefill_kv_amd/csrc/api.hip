@@ -227,6 +227,10 @@ Workspace workspace_layout(const Problem& p) {
   w.gtcount = take((size_t)p.Hkv * p.NKT * 4);
   w.select_end = o;
   w.selidx = take(SH * p.kv_budget * 4);
+  // the attention runs after the selection: its partial states reuse the
+  // selection's scratch when they fit there (never the kept indices)
+  const size_t attn = attn_workspace_bytes(p);
+  w.attn = attn <= w.select_end ? 0 : take(attn);
   w.total = o;
   return w;
 }
@@ -288,6 +292,18 @@ quoka_status static_scratch(char** out) {
     addr[dev] = (char*)ptr;
   }
   *out = addr[dev];
+  return QUOKA_OK;
+}
+
+// The attention entry points' workspace: needed only when the shape splits
+// its keys (attn_workspace_bytes > 0).
+quoka_status attn_ws_check(const Problem& p, const void* ws, size_t ws_bytes) {
+  const size_t need = attn_workspace_bytes(p);
+  if (need == 0) return QUOKA_OK;
+  if (!ws) return fail(QUOKA_EWORKSPACE, "this shape needs %zu bytes of workspace, none given", need);
+  if (!aligned16(ws)) return fail(QUOKA_EINVAL, "workspace is not 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   return QUOKA_OK;
 }
 
@@ -387,10 +403,21 @@ quoka_status quoka_gather(const quoka_shape* shape, const void* k_hist, const vo
                    stream);
 }
 
+quoka_status quoka_attn_workspace_bytes(const quoka_shape* shape, int32_t kv_budget,
+                                        size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(QUOKA_EINVAL, "bytes is null");
+  Problem p;
+  quoka_status rc = make_problem(shape, 1, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  *bytes = attn_workspace_bytes(p);
+  return QUOKA_OK;
+}
+
 quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q, const void* k_sel,
                               const void* v_sel, int32_t kv_budget, const void* k_chunk,
-                              const void* v_chunk, float softmax_scale, void* out,
-                              hipStream_t stream) {
+                              const void* v_chunk, float softmax_scale, void* out, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   Problem p;
   quoka_status rc = make_problem(shape, 1, kv_budget, &p);
@@ -402,16 +429,18 @@ quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q, const voi
   QUOKA_NEED(v_chunk, p.TC);
   QUOKA_NEED(out, p.TC);
   if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
+  if ((rc = attn_ws_check(p, ws, ws_bytes))) return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
   return hip_check(
-      launch_attention(p, q, k_sel, v_sel, nullptr, k_chunk, v_chunk, scale, out, stream),
+      launch_attention(p, q, k_sel, v_sel, nullptr, k_chunk, v_chunk, scale, out, ws, stream),
       "attention", stream);
 }
 
 quoka_status quoka_chunk_attn_gather(const quoka_shape* shape, const void* q, const void* k_hist,
                                      const void* v_hist, const int32_t* sel_idx,
                                      int32_t kv_budget, const void* k_chunk, const void* v_chunk,
-                                     float softmax_scale, void* out, hipStream_t stream) {
+                                     float softmax_scale, void* out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
   g_err[0] = 0;
   Problem p;
   quoka_status rc = make_problem(shape, 1, kv_budget, &p);
@@ -424,9 +453,10 @@ quoka_status quoka_chunk_attn_gather(const quoka_shape* shape, const void* q, co
   QUOKA_NEED(v_chunk, p.TC);
   QUOKA_NEED(out, p.TC);
   if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
+  if ((rc = attn_ws_check(p, ws, ws_bytes))) return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
   return hip_check(
-      launch_attention(p, q, k_hist, v_hist, sel_idx, k_chunk, v_chunk, scale, out, stream),
+      launch_attention(p, q, k_hist, v_hist, sel_idx, k_chunk, v_chunk, scale, out, ws, stream),
       "attention", stream);
 }
 
@@ -456,9 +486,9 @@ quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q, const 
   rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
   if (rc != QUOKA_OK) return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
-  return hip_check(
-      launch_attention(p, q, k_hist, v_hist, sel, k_chunk, v_chunk, scale, out, stream),
-      "attention", stream);
+  return hip_check(launch_attention(p, q, k_hist, v_hist, sel, k_chunk, v_chunk, scale, out,
+                                   base + w.attn, stream),
+                   "attention", stream);
 }
 
 quoka_status quoka_prefill_chunk_static(const quoka_shape* shape, const void* q,
@@ -490,9 +520,9 @@ quoka_status quoka_prefill_chunk_static(const quoka_shape* shape, const void* q,
   rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
   if (rc != QUOKA_OK) return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
-  return hip_check(
-      launch_attention(p, q, k_hist, v_hist, sel, k_chunk, v_chunk, scale, out, stream),
-      "attention", stream);
+  return hip_check(launch_attention(p, q, k_hist, v_hist, sel, k_chunk, v_chunk, scale, out,
+                                   base + w.attn, stream),
+                   "attention", stream);
 }
 
 }  // extern "C"
@@ -596,7 +626,8 @@ quoka_status quoka_prefill_prompt(const quoka_prompt* prompt, const void* q, con
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
     if ((rc = hip_check(launch_attention(p, qi, k, v, sel, (const char*)k + (size_t)a * krow,
                                          (const char*)v + (size_t)a * krow, scale,
-                                         (char*)out + (size_t)a * qrow, stream),
+                                         (char*)out + (size_t)a * qrow,
+                                         base + lay.chunk_ws + w.attn, stream),
                         "attention", stream)))
       return rc;
   }

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
 constexpr int kXcds = 8;
 
 constexpr int kAttnKeys = 64;  // keys per K/V tile
+constexpr int64_t kAttnMaxSplit = 8;  // key ranges per row tile, at most
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const int32_t* __restrict__ sel, const bf16* __restrict__ k_chunk, const bf16* __restrict__ v_chunk,
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int S, int Hq,
     int Hkv, int G, int kv_budget, int ntile_max, int pair_order, float scale_log2,
-    bf16* __restrict__ out) {
+    int nsplit, float* __restrict__ part_o, float2* __restrict__ part_ml, bf16* __restrict__ out) {
   constexpr int KT = kAttnKeys, NDS = D / 16, NDB = D / 32;
   // K and V tiles land straight from global memory (buffer loads into LDS),
   // two buffers each, unpadded 2D-byte rows with XOR-swizzled 16-byte chunks
@@ -155,12 +156,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Vs1[KT * D];
 
   // XCD-aware renumbering: linear block L runs on XCD L % 8; give XCD x a
-  // contiguous range of logical ids (tile-fastest, then head, then sequence).
+  // contiguous range of logical ids (key range fastest, then tile, then head,
+  // then sequence). ntile_max counts (tile, key range) units.
   const int nblk = ntile_max * Hkv * S;
   const int L = blockIdx.x;
   const int qx = nblk / kXcds, rx = nblk % kXcds, x = L % kXcds, slot = L / kXcds;
   const int logical = x < rx ? x * (qx + 1) + slot : rx * (qx + 1) + (x - rx) * qx + slot;
-  const int bx = logical % ntile_max;
+  const int bxs = logical % ntile_max;
+  const int bx = bxs / nsplit, sigma = bxs % nsplit;
   const int h = (logical / ntile_max) % Hkv;
   const int s = logical / (ntile_max * Hkv);
 
@@ -231,6 +234,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   const bf16* v2 = v_chunk + ((int64_t)c_off * Hkv + h) * D;
   const int n1 = (B_eff + KT - 1) / KT;
   const int n_all = n1 + (t_last + KT) / KT;
+  // with nsplit > 1 this workgroup takes the sigma-th of nsplit near-equal
+  // ranges of the n_all key tiles
+  const int it0 = (int)((int64_t)sigma * n_all / nsplit);
+  const int it1 = (int)((int64_t)(sigma + 1) * n_all / nsplit);
   const uint32_t rb1 = kIdx ? (uint32_t)Hkv * D * 2u : D * 2u;           // row bytes
   const uint32_t rb2 = (uint32_t)Hkv * D * 2u;
   const uint32_t end1 = kIdx ? (Lh > 0 ? (uint32_t)(Lh - 1) * rb1 + D * 2u : 0u)  // valid bytes
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
       nidx[u] = key < B_eff ? sidx[key] : -1;
     }
   };
-  if (kIdx && n1 > 0) fetch_idx(0);
+  if (kIdx && it0 < n1) fetch_idx(it0);
   using lds_ptr = __attribute__((address_space(3))) void*;
   auto load = [&](int it, bf16* kd, bf16* vd) __attribute__((always_inline)) {
     const bool ph1 = it < n1;
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(base + vcol[u]), 0, 0, 0);
     }
   };
-  load(0, Ks0, Vs0);
+  if (it0 < it1) load(it0, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -321,12 +328,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   }
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
-  auto step = [&, B_eff, t_wave_first, t_wave_last, n1, n_all, t](int it, auto Bc)
+  auto step = [&, B_eff, t_wave_first, t_wave_last, n1, it1, t](int it, auto Bc)
                   __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
     bf16* kcur = B ? Ks1 : Ks0;
     bf16* vcur = B ? Vs1 : Vs0;
-    if (it + 1 < n_all) load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
+    if (it + 1 < it1) load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
     const bf16* ks = kcur;
@@ -386,7 +393,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
-    const float base = m_run * scale_log2;
+    // a row with no visible key yet (its key range starts past its token)
+    // keeps p = 0 instead of exp2(-inf + inf)
+    const float base = m_run == -INFINITY ? 0.f : m_run * scale_log2;
     bf16x8 pb[2][2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -432,14 +441,33 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int it = 0; it < n_all; it += 2) {
+  for (int it = it0; it < it1; it += 2) {
     step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_all) step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 1 < it1) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   uint32_t la, lb;
   swap32(__float_as_uint(l_part), la, lb);  // the two lane halves of each query column
   const float l_run = __uint_as_float(la) + __uint_as_float(lb);
+  if (nsplit > 1) {
+    // this key range's unnormalised state: O, and (reference max in log2
+    // units, row sum), combined with the other ranges' by attn_merge_kernel
+    if (rvalid) {
+      const int64_t nrow = (int64_t)cu_chunk[S] * Hq;
+      const int64_t grow = (int64_t)(c_off + t) * Hq + jh;
+      float* po = part_o + ((int64_t)sigma * nrow + grow) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(f32x4*)(po + db * 32 + hi * 4 + 8 * i) =
+              (f32x4){oacc[db][i * 4], oacc[db][i * 4 + 1], oacc[db][i * 4 + 2], oacc[db][i * 4 + 3]};
+      if (hi == 0)
+        part_ml[sigma * nrow + grow] =
+            make_float2(m_run == -INFINITY ? -INFINITY : m_run * scale_log2, l_run);
+    }
+    return;
+  }
   if (rvalid) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
     bf16* orow = out + ((int64_t)(c_off + t) * Hq + jh) * D;
@@ -455,6 +483,43 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   }
 }
 
+// Combination of the key ranges' states of a row (the online softmax's merge
+// step): with b = the largest reference max (log2 units),
+// O = sum_r 2^(b_r - b) O_r / sum_r 2^(b_r - b) l_r. A range that saw no key
+// of the row (b_r = -inf) adds nothing. One thread per 8 outputs of a row.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                         const float2* __restrict__ part_ml,
+                                                         int nsplit, int64_t nrow,
+                                                         bf16* __restrict__ out) {
+  constexpr int CPR = D / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = i / CPR;
+  const int c = (int)(i % CPR);
+  if (row >= nrow) return;
+  float b = -INFINITY;
+  for (int r = 0; r < nsplit; ++r) b = fmaxf(b, part_ml[r * nrow + row].x);
+  float l = 0.f;
+  f32x4 a0 = {}, a1 = {};
+  for (int r = 0; r < nsplit; ++r) {
+    const float2 ml = part_ml[r * nrow + row];
+    if (ml.x == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(ml.x - b);
+    l = fmaf(w, ml.y, l);
+    const f32x4* po = (const f32x4*)(part_o + (r * nrow + row) * D + c * 8);
+    a0 += w * po[0];
+    a1 += w * po[1];
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = (bf16)(a0[e] * inv);
+    v[4 + e] = (bf16)(a1[e] * inv);
+  }
+  *(bf16x8*)(out + row * D + c * 8) = v;
+}
+
 // Eight-wave workgroups share each K/V tile between twice the rows (half the
 // LDS writes and L2 reads per row) but hold twice the rows, so a shape has
 // half as many of them; they are used when that still leaves two per CU
@@ -464,34 +529,85 @@ constexpr int kAttnWideMinBlocks = 512;
 // registers), 256 CUs.
 constexpr int kAttnResident4 = 2 * 256;
 
+namespace {
+
+struct AttnPlan {
+  int nw, pair, ntile, nsplit;
+};
+
+AttnPlan attn_plan(const Problem& p) {
+  const int64_t rows = (int64_t)p.maxC * p.G;
+  const int64_t n128 = (rows + 127) / 128;
+  const int64_t grid4 = n128 * p.Hkv * p.S;  // four-wave workgroups the shape needs
+  // eight waves on 256 contiguous rows when that still leaves two workgroups
+  // per CU; eight waves on a heavy and a light 128-row tile when four-wave
+  // workgroups would fill the chip exactly once (then pairing balances the
+  // CUs and shares the K/V loads); else four waves
+  const bool wide = (rows + 255) / 256 * p.Hkv * p.S >= kAttnWideMinBlocks;
+  const int pair = (!wide && grid4 > 256 && grid4 <= kAttnResident4) ? 1 : 0;
+  const int nw = (wide || pair) ? 8 : 4;
+  const int ntile = (int)(nw == 8 ? (n128 + 1) / 2 : n128);
+  // at most half the CUs busy (few rows: short chunks, decode): split each
+  // tile's key tiles into ranges, about one workgroup per CU, and merge the
+  // ranges' states afterwards. Measured on the narrow layer (224 workgroups)
+  // a split gained nothing: the partial states' HBM round trip cost what the
+  // balance won, so the rule stops at half the chip.
+  int nsplit = 1;
+  if (nw == 4 && grid4 <= 128) {
+    const int64_t steps = (p.kv_budget + 63) / 64 + (p.maxC + 63) / 64;
+    nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({256 / grid4, steps, kAttnMaxSplit}));
+  }
+  return {nw, pair, ntile, nsplit};
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(const Problem& p) {
+  if (p.dtype != QUOKA_BF16 || p.maxC == 0) return 0;
+  const AttnPlan a = attn_plan(p);
+  if (a.nsplit == 1) return 0;
+  const size_t nrow = (size_t)p.TC * p.Hq;
+  return (size_t)a.nsplit * nrow * ((size_t)p.D * 4 + 8);
+}
+
 hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
                             const void* v_sel, const int32_t* sel, const void* k_chunk,
-                            const void* v_chunk, float scale, void* out, hipStream_t st) {
+                            const void* v_chunk, float scale, void* out, void* attn_ws,
+                            hipStream_t st) {
   if (p.maxC == 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (p.dtype == QUOKA_BF16) {
-    const int64_t rows = (int64_t)p.maxC * p.G;
-    const int64_t n128 = (rows + 127) / 128;
-    const int64_t grid4 = n128 * p.Hkv * p.S;  // four-wave workgroups the shape needs
-    // eight waves on 256 contiguous rows when that still leaves two workgroups
-    // per CU; eight waves on a heavy and a light 128-row tile when four-wave
-    // workgroups would fill the chip exactly once (then pairing balances the
-    // CUs and shares the K/V loads); else four waves
-    const bool wide = (rows + 255) / 256 * p.Hkv * p.S >= kAttnWideMinBlocks;
-    const int pair = (!wide && grid4 > 256 && grid4 <= kAttnResident4) ? 1 : 0;
-    const int nw = (wide || pair) ? 8 : 4;
-    const int ntile = (int)(nw == 8 ? (n128 + 1) / 2 : n128);
-    dim3 grid((unsigned)(ntile * p.Hkv * p.S));
+    const AttnPlan a = attn_plan(p);
+    const int nw = a.nw, pair = a.pair, ntile = a.ntile, nsplit = a.nsplit;
+    const int64_t nrow = (int64_t)p.TC * p.Hq;
+    float* part_o = nullptr;
+    float2* part_ml = nullptr;
+    if (nsplit > 1) {
+      if (!attn_ws) return hipErrorInvalidValue;
+      part_o = (float*)attn_ws;
+      part_ml = (float2*)(part_o + (size_t)nsplit * nrow * p.D);
+    }
+    dim3 grid((unsigned)(ntile * nsplit * p.Hkv * p.S));
 #define QUOKA_ATTN(D, NW, IDX)                                                                 \
   hipLaunchKernelGGL((attn_mfma_kernel<D, NW, IDX>), grid, dim3(NW * 64), 0, st, (const bf16*)q, \
                      (const bf16*)k_sel, (const bf16*)v_sel, sel, (const bf16*)k_chunk,           \
                      (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,          \
-                     p.kv_budget, ntile, pair, sl2, (bf16*)out)
+                     p.kv_budget, ntile * nsplit, pair, sl2, nsplit, part_o, part_ml, (bf16*)out)
 #define QUOKA_ATTN_NW(D, IDX) { if (nw == 8) QUOKA_ATTN(D, 8, IDX); else QUOKA_ATTN(D, 4, IDX); }
     if (sel) { if (p.D == 128) QUOKA_ATTN_NW(128, true) else QUOKA_ATTN_NW(64, true) }
     else     { if (p.D == 128) QUOKA_ATTN_NW(128, false) else QUOKA_ATTN_NW(64, false) }
 #undef QUOKA_ATTN_NW
 #undef QUOKA_ATTN
+    if (nsplit > 1) {
+      const int64_t nthr = nrow * (p.D / 8);
+      dim3 mg((unsigned)((nthr + 255) / 256));
+      if (p.D == 128)
+        hipLaunchKernelGGL(attn_merge_kernel<128>, mg, dim3(256), 0, st, part_o, part_ml, nsplit,
+                           nrow, (bf16*)out);
+      else
+        hipLaunchKernelGGL(attn_merge_kernel<64>, mg, dim3(256), 0, st, part_o, part_ml, nsplit,
+                           nrow, (bf16*)out);
+    }
   } else {
     dim3 grid((unsigned)((p.maxC + 63) / 64), (unsigned)p.Hq, (unsigned)p.S);
 #define QUOKA_ATTN(D)                                                                       \

@@ -72,6 +72,8 @@ struct Workspace {
   size_t qkey;      // uint64 [Hkv, TC] tokens re-ranked in fp64
   size_t row0;      // double [S, Hkv, D] the one-row baselines' row in fp64
   size_t selidx;    // int32 [S, Hkv, B]  (prefill path)
+  size_t attn;      // the attention's partial states (after the selection;
+                    // over its scratch when they fit there)
   size_t select_end, total;
   size_t zero_begin, zero_end;  // [hist .. chcount] region cleared per call
 };
@@ -129,9 +131,15 @@ hipError_t launch_gather(const Problem& p, const void* k_hist, const void* v_his
 // sel == nullptr: history rows are k_sel / v_sel [S, Hkv, kv_budget, D];
 // otherwise k_sel / v_sel are k_hist / v_hist and row b of (s, h) is history
 // row sel[s, h, b] (gather fused into the attention).
+// Shapes that fill at most half the chip split each row tile's keys into
+// ranges whose partial softmax states (fp32 O, max, sum per row and range) go
+// to attn_ws, attn_workspace_bytes(p) bytes (0: no split, attn_ws unused),
+// and are merged by a second launch.
+size_t attn_workspace_bytes(const Problem& p);
 hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
                             const void* v_sel, const int32_t* sel, const void* k_chunk,
-                            const void* v_chunk, float scale, void* out, hipStream_t st);
+                            const void* v_chunk, float scale, void* out, void* attn_ws,
+                            hipStream_t st);
 
 // Per-chunk offsets {0, C_i, 0, L_i} of a one-sequence prompt split in chunks.
 hipError_t launch_prompt_offsets(int T, int chunk_len, int nch, int32_t* cu, hipStream_t st);

@@ -92,7 +92,9 @@ typedef struct quoka_shape {
 #define QUOKA_MAX_Q_BUDGET 128
 
 /* Bytes of device workspace quoka_select / quoka_prefill_chunk need for this
- * shape and these budgets (written to *bytes). */
+ * shape and these budgets (written to *bytes); they include the attention's
+ * partial states (quoka_attn_workspace_bytes), which quoka_prefill_chunk keeps
+ * there, so the same workspace also serves quoka_chunk_attn(_gather). */
 quoka_status quoka_workspace_bytes(const quoka_shape* shape, int32_t q_budget,
                                    int32_t kv_budget, size_t* bytes);
 
@@ -185,16 +187,33 @@ quoka_status quoka_gather(const quoka_shape* shape, const void* k_hist,
                           int32_t kv_budget, void* k_sel, void* v_sel,
                           hipStream_t stream);
 
+/* Bytes of device workspace quoka_chunk_attn / quoka_chunk_attn_gather need
+ * for this shape (written to *bytes). Shapes whose bf16 attention fills at
+ * most half the chip (short chunks, decode steps) split each query tile's
+ * keys into ranges computed by separate workgroups: softmax is shift
+ * invariant, so the ranges' partial states (unnormalised O, running max, row
+ * sum, fp32) combine exactly into the row's result ("Background > Chunked
+ * prefill": each query attends to the kept history and its causal prefix,
+ * in any order of the keys). Those states need nsplit * T_c * H_q * (4 d + 8)
+ * bytes; every other shape needs 0. */
+quoka_status quoka_attn_workspace_bytes(const quoka_shape* shape,
+                                        int32_t kv_budget, size_t* bytes);
+
 /* Chunk attention: step 4 ("Background > Chunked prefill"; "QUOKA Method":
  * the reduced KV set goes to a dense attention kernel). Query row (t, j) of
  * sequence s attends to the first B_eff rows of k_sel / v_sel[s, j / G] and to
  * the chunk's keys 0..t (diagonal included).
- *   softmax_scale <= 0 selects 1 / sqrt(d). */
+ *   softmax_scale <= 0 selects 1 / sqrt(d).
+ *   ws, ws_bytes  device workspace of at least quoka_attn_workspace_bytes()
+ *                 bytes (may be null when that is 0), 16-byte aligned; its
+ *                 contents on entry do not matter. Too small:
+ *                 QUOKA_EWORKSPACE. */
 quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q,
                               const void* k_sel, const void* v_sel,
                               int32_t kv_budget, const void* k_chunk,
                               const void* v_chunk, float softmax_scale,
-                              void* out, hipStream_t stream);
+                              void* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /* Gather and chunk attention in one pass (the gather fused into the
  * attention: the same result as quoka_gather followed by quoka_chunk_attn,
@@ -202,13 +221,14 @@ quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q,
  * (s, h) are rows sel_idx[s, h, 0 .. B_eff) of sequence s, head h of k_hist /
  * v_hist; an index of -1 (or outside [0, L_s)) contributes a zero key and a
  * zero value, exactly as quoka_gather's zero rows would.
- *   softmax_scale <= 0 selects 1 / sqrt(d). */
+ *   softmax_scale <= 0 selects 1 / sqrt(d); ws, ws_bytes as for
+ *   quoka_chunk_attn. */
 quoka_status quoka_chunk_attn_gather(const quoka_shape* shape, const void* q,
                                      const void* k_hist, const void* v_hist,
                                      const int32_t* sel_idx, int32_t kv_budget,
                                      const void* k_chunk, const void* v_chunk,
-                                     float softmax_scale, void* out,
-                                     hipStream_t stream);
+                                     float softmax_scale, void* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
 
 /* The whole hot path (select, then attention with the gather fused in) in
  * one call. sel_idx_opt, when not null, receives the kept indices as in

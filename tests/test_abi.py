@@ -108,16 +108,50 @@ def test_null_and_misaligned_inputs_are_rejected(lib):
     st = lib.quoka_prefill_chunk(ctypes.byref(shape.c), None, p, p, p, p, 4, 8, 0.0, p, None, p,
                                  1 << 30, None)
     assert st == cpk.QUOKA_EINVAL and "q is null" in lib.quoka_last_error().decode()
-    st = lib.quoka_chunk_attn(ctypes.byref(shape.c), p + 2, p, p, 8, p, p, 0.0, p, None)
+    st = lib.quoka_chunk_attn(ctypes.byref(shape.c), p + 2, p, p, 8, p, p, 0.0, p, None, 0, None)
     assert st == cpk.QUOKA_EINVAL and "aligned" in lib.quoka_last_error().decode()
-    st = lib.quoka_chunk_attn(ctypes.byref(shape.c), p, p, p, 8, p, p, float("nan"), p, None)
+    st = lib.quoka_chunk_attn(ctypes.byref(shape.c), p, p, p, 8, p, p, float("nan"), p, None, 0, None)
     assert st == cpk.QUOKA_EINVAL
     st = lib.quoka_gather(ctypes.byref(shape.c), p, p, None, 8, p, p, None)
     assert st == cpk.QUOKA_EINVAL
-    st = lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), p, p, p, None, 8, p, p, 0.0, p, None)
+    st = lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), p, p, p, None, 8, p, p, 0.0, p, None, 0, None)
     assert st == cpk.QUOKA_EINVAL and "sel_idx is null" in lib.quoka_last_error().decode()
-    st = lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), p, p, p + 4, p, 8, p, p, 0.0, p, None)
+    st = lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), p, p, p + 4, p, 8, p, p, 0.0, p, None, 0, None)
     assert st == cpk.QUOKA_EINVAL and "aligned" in lib.quoka_last_error().decode()
+
+
+def _attn_ws(shape, kvb):
+    n = ctypes.c_size_t(0)
+    st = cpk.load_library().quoka_attn_workspace_bytes(ctypes.byref(shape.c), kvb, ctypes.byref(n))
+    return st, n.value
+
+
+def test_attention_workspace_only_for_shapes_that_split_their_keys(lib):
+    # decode: 8 sequences of one token, 64 (sequence, KV head) tiles on 256 CUs
+    dec = _host_shape(list(range(9)), [16384 * i for i in range(9)], hq=32, hkv=8)
+    st, n = _attn_ws(dec, 2048)
+    # four key ranges: 8 * 32 rows, 4 * 128 + 8 bytes each per range
+    assert st == 0 and n == 4 * 8 * 32 * (4 * 128 + 8)
+    # a 2048-token chunk with 8 KV heads fills the chip: no split, no workspace
+    big = _host_shape([0, 2048], [0, 32768], hq=32, hkv=8)
+    assert _attn_ws(big, 2048) == (0, 0)
+    # fp32 runs the VALU kernel, which never splits
+    assert _attn_ws(_host_shape(list(range(9)), [16384 * i for i in range(9)], hq=32, hkv=8,
+                                dtype="fp32"), 2048) == (0, 0)
+    # the per-chunk workspace covers the attention's states as well
+    st, nsel = _ws_status(dec, 1, 2048)
+    assert st == 0 and nsel >= n
+
+
+def test_split_attention_without_workspace_is_rejected(lib):
+    shape = _host_shape(list(range(9)), [16384 * i for i in range(9)], hq=32, hkv=8)
+    buf = np.zeros(4096, np.uint8)
+    p = buf.ctypes.data + (16 - buf.ctypes.data % 16) % 16
+    st = lib.quoka_chunk_attn(ctypes.byref(shape.c), p, p, p, 2048, p, p, 0.0, p, None, 0, None)
+    assert st == cpk.QUOKA_EWORKSPACE and "needs" in lib.quoka_last_error().decode()
+    st = lib.quoka_chunk_attn_gather(ctypes.byref(shape.c), p, p, p, p, 2048, p, p, 0.0, p, p, 64,
+                                     None)
+    assert st == cpk.QUOKA_EWORKSPACE and "needs" in lib.quoka_last_error().decode()
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):

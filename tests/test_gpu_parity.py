@@ -2,7 +2,9 @@
 finishes in seconds (several tiles per kernel plus ragged tails), and the edge
 cases: empty history, one-token chunk, budgets above the data, the largest
 query budget, zero vectors, head_dim 64 and 128, GQA groups of 1, 2, 4, 7 and 8,
-and decode-like batches (every chunk one or two tokens).
+and decode-like batches (every chunk one or two tokens). The small bf16 cases
+run the attention with each tile's keys split into ranges (a key range that
+starts past some rows' tokens included) and merged; one case runs it unsplit.
 """
 import math
 
@@ -36,6 +38,9 @@ CASES = {
     "bf16_decode_g4": ([(1, 3000), (1, 0), (2, 500), (1, 64)], 8, 2, 128, "bf16", 1, 256, {}),
     "bf16_decode_g8": ([(1, 1500), (1, 70)], 16, 2, 128, "bf16", 2, 1000, dict(scaled=True)),
     "bf16_decode_d64_g1": ([(1, 2000), (1, 100), (1, 1)], 2, 2, 64, "bf16", 1, 300, {}),
+    # 140 four-wave attention tiles: the unsplit four-wave order (at most 128
+    # tiles split their keys into ranges and merge, as every smaller case here)
+    "bf16_four_wave_unsplit": ([(1100, 1500)], 16, 4, 128, "bf16", 16, 200, {}),
     # scorer tiles of 1024 keys (four streamed blocks per wave), last tile partial
     "bf16_scorer_tiles_1024": ([(64, 33000)], 8, 8, 128, "bf16", 16, 512, {}),
     # scorer tiles of 512 keys: many short histories, some waves with one block
@@ -179,6 +184,13 @@ ORDER_CASES = {
     # the same two orders with head_dim 64 (K/V tiles of 8 rows per 1 KB LDS piece)
     "pair_odd_d64": ([(1056, 3000)], 32, 8, 64, "bf16", 16, 512),
     "wide_odd_d64": ([(1056, 600)] * 8, 32, 8, 64, "bf16", 8, 256),
+    # four 128-row tiles: each tile's keys split into 8 ranges (mostly history),
+    # merged afterwards
+    "split8_history": ([(64, 8000)], 8, 2, 128, "bf16", 16, 1024),
+    # 20 tiles, 6 ranges over 2..6 key tiles: ranges inside the chunk start past
+    # the tokens of a tile's first rows (those rows see no key in them), and the
+    # short tiles leave some ranges empty
+    "split6_chunk": ([(300, 100)], 8, 2, 128, "bf16", 8, 64),
     # GQA 7: 128-row tiles cut through a token's heads (paired order, 66 tiles)
     "pair_g7": ([(1200, 3000)], 28, 4, 128, "bf16", 16, 512),
     # one query head per KV head in the wide order, chunks of different lengths
