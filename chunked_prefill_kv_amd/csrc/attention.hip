@@ -381,10 +381,13 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     { const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
       mx = fmaxf(mx, fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1]))); }
     // lazy rescaling: the reference max moves only when the tile's max
-    // exceeds it by more than 2^8 in the exponent, so p <= 256 and the output
-    // is rescaled on few tiles (exact either way)
+    // exceeds it by more than 32 in log2 units, so p <= 2^32 (fp32 and bf16
+    // hold that with their usual relative precision; row sums stay far below
+    // the fp32 range) and the output is rescaled on few tiles (exact either
+    // way). On the channel-scaled layer data a bound of 8 rescaled often
+    // enough to cost 2-5 % of the kernel.
     const float m_cand = fmaxf(m_run, mx);
-    const bool upd = (m_cand - m_run) * scale_log2 > 8.0f;
+    const bool upd = (m_cand - m_run) * scale_log2 > 32.0f;
     if (__ballot(upd)) {
       const float m_new = upd ? m_cand : m_run;
       const float alpha = upd ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
