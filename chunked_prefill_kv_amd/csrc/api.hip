@@ -123,10 +123,22 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
     const int64_t L = (int64_t)sh->cu_hist_host[s + 1] - sh->cu_hist_host[s];
     if (C < 0 || L < 0)
       return fail(QUOKA_EINVAL, "cu offsets decrease at sequence %d", s);
-    p->NQT += (C + kQprepTokens - 1) / kQprepTokens;
     p->NKT += (L + kTopbKeys - 1) / kTopbKeys;
     p->maxC = std::max<int>(p->maxC, (int)C);
     p->maxL = std::max<int>(p->maxL, (int)L);
+  }
+  // Query-prep tiles of 64 tokens (4 per wave), or of 32 or 16 when that
+  // leaves fewer workgroups than CUs (short chunks, few KV heads): the
+  // query side then spreads over the chip instead of a few long workgroups.
+  p->qtok = kQprepTokens;
+  for (;;) {
+    p->NQT = 0;
+    for (int s = 0; s < S; ++s) {
+      const int64_t C = (int64_t)sh->cu_chunk_host[s + 1] - sh->cu_chunk_host[s];
+      p->NQT += (C + p->qtok - 1) / p->qtok;
+    }
+    if (p->qtok == kQprepTokens / 4 || p->NQT * p->Hkv >= 256) break;
+    p->qtok /= 2;
   }
   // Scorer tiles: one 64-key block per wave while that takes at most two
   // rounds of workgroups; past that each wave streams several blocks with

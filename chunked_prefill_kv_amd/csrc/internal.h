@@ -11,7 +11,8 @@
 namespace quoka {
 
 // Tilings (all per sequence; tiles never straddle two sequences).
-constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup
+constexpr int kQprepTokens = 64;     // tokens per query-prep workgroup, at most
+constexpr int kQprepWavesTotal = 16; // waves per query-prep workgroup
 constexpr int kScoreKeysMin = 256;   // history keys per scorer workgroup: one block per wave...
 constexpr int kScoreKeysMax = 2048;  // ...up to eight blocks per wave, streamed
 constexpr int kScoreMaxBlocks = 512; // one round of scorer workgroups (two per CU)
@@ -35,6 +36,7 @@ struct Problem {
   const int32_t* cu_hist_h;  // host
   int64_t TC, TL;            // total chunk tokens, total history keys
   int64_t NQT, NSB, NKT;     // total qprep / scorer / top-B tiles over sequences
+  int qtok;                  // tokens per query-prep tile: 64, 32 or 16
   int maxC, maxL;            // longest chunk, longest history
   int q_budget, kv_budget, nq_pad;
   int score_keys;            // history keys per scorer workgroup (a power of two, 256..2048)

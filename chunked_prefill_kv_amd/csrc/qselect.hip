@@ -23,7 +23,7 @@ namespace quoka {
 // ---------------------------------------------------------------------------
 // Tile prefix sums of the three tilings, by one thread.
 __device__ void write_plan(const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist,
-                           int S, int score_keys, int32_t* __restrict__ plan) {
+                           int S, int qtok, int score_keys, int32_t* __restrict__ plan) {
   int32_t* qt = plan;
   int32_t* sb = plan + (S + 1);
   int32_t* kt = plan + 2 * (S + 1);
@@ -32,7 +32,7 @@ __device__ void write_plan(const int32_t* __restrict__ cu_chunk, const int32_t* 
     qt[s] = a; sb[s] = b; kt[s] = c;
     const int C = cu_chunk[s + 1] - cu_chunk[s];
     const int L = cu_hist[s + 1] - cu_hist[s];
-    a += (C + kQprepTokens - 1) / kQprepTokens;
+    a += (C + qtok - 1) / qtok;
     b += (L + score_keys - 1) / score_keys;
     c += (L + kTopbKeys - 1) / kTopbKeys;
   }
@@ -43,25 +43,24 @@ __device__ void write_plan(const int32_t* __restrict__ cu_chunk, const int32_t* 
 // and clears, has no workgroup).
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu_chunk,
                                                    const int32_t* __restrict__ cu_hist, int S,
-                                                   int score_keys, int32_t* __restrict__ plan,
+                                                   int qtok, int score_keys, int32_t* __restrict__ plan,
                                                    uint4* __restrict__ zero, int64_t nzero16) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nzero16;
        i += (int64_t)gridDim.x * blockDim.x)
     zero[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (blockIdx.x == 0 && threadIdx.x == 0) write_plan(cu_chunk, cu_hist, S, score_keys, plan);
+  if (blockIdx.x == 0 && threadIdx.x == 0) write_plan(cu_chunk, cu_hist, S, qtok, score_keys, plan);
 }
 
 
 // ---------------------------------------------------------------------------
 // K1a: g_t = mean_j unit(q_{t,j}) over the G query heads of KV head h, for a
-// tile of 64 tokens; also the tile's fp64 sum of g (for the mean query).
-// 16 waves; each wave owns 4 tokens and issues all their row loads before
-// reducing. A head row is spread over D / 4 lanes (4 elements each), so one
+// tile of 16 kTokPerWave tokens (64, or 32 / 16 for shapes with few tiles);
+// also the tile's fp64 sum of g (for the mean query). 16 waves; each wave
+// owns kTokPerWave tokens and issues all their row loads before reducing. A head row is spread over D / 4 lanes (4 elements each), so one
 // load instruction covers 256 / D rows; the arithmetic is fp64.
 // ---------------------------------------------------------------------------
-constexpr int kQprepThreads = 1024;
-constexpr int kQprepWaves = kQprepThreads / 64;
-constexpr int kTokPerWave = kQprepTokens / kQprepWaves;  // 4
+constexpr int kQprepThreads = kQprepWavesTotal * 64;
+constexpr int kQprepWaves = kQprepWavesTotal;
 
 // 4 consecutive elements as fp32 (one 8- or 16-byte load).
 template <typename T>
@@ -88,7 +87,7 @@ __device__ __forceinline__ double head_group_sum(double v) {
   return RL == 32 ? pair32_sum(v) : rows_sum(v);
 }
 
-template <typename T, int D>
+template <typename T, int D, int kTokPerWave>
 __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     const T* __restrict__ q, const int32_t* __restrict__ cu_chunk,
     const int32_t* __restrict__ cu_hist, int S, int Hq, int Hkv, int G, float* __restrict__ g,
@@ -97,6 +96,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
   constexpr int EPL = 4;       // elements per lane
   constexpr int RL = D / EPL;  // lanes per head row: 32 or 16
   constexpr int RPI = 64 / RL; // head rows per load instruction
+  constexpr int kQprepTok = kQprepWaves * kTokPerWave;  // tokens per tile
   const int tile = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the plan and the cleared counters are for the later kernels
@@ -105,13 +105,14 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
     for (int64_t i = ((int64_t)h * gridDim.x + tile) * kQprepThreads + threadIdx.x; i < nzero16;
          i += nb * kQprepThreads)
       zero[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (tile == 0 && h == 0 && threadIdx.x == 0) write_plan(cu_chunk, cu_hist, S, score_keys, plan);
+    if (tile == 0 && h == 0 && threadIdx.x == 0)
+      write_plan(cu_chunk, cu_hist, S, kQprepTok, score_keys, plan);
   }
   // this tile's sequence: wave prefix sums over the sequences' tile counts
   int s = 0, t_base = 0;
   for (int s0 = 0, acc = 0; s0 < S; s0 += 64) {
     const int sq = s0 + lane;
-    const int n = sq < S ? (cu_chunk[sq + 1] - cu_chunk[sq] + kQprepTokens - 1) / kQprepTokens : 0;
+    const int n = sq < S ? (cu_chunk[sq + 1] - cu_chunk[sq] + kQprepTok - 1) / kQprepTok : 0;
     const int incl = (int)wave_inclusive_scan((uint32_t)n);
     const int excl = incl - n;
     const uint64_t m = __ballot(n > 0 && acc + excl <= tile && tile < acc + incl);
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
   const int c_off = cu_chunk[s];
   const int C = cu_chunk[s + 1] - c_off;
   const int grp = lane / RL, sub = lane % RL;
-  const int tw = (tile - t_base) * kQprepTokens + wave * kTokPerWave;
+  const int tw = (tile - t_base) * kQprepTok + wave * kTokPerWave;
 
   // the unit head rows and their mean over the group in fp64, so that the
   // tile sums (hence the mean query) and the stored g (rounded once to fp32)
@@ -345,12 +346,12 @@ __device__ __forceinline__ void load8(const T* __restrict__ p, float (&x)[8]) {
 }
 
 // ---------------------------------------------------------------------------
-// K1b: c_t = cos(M, g_t) for a tile of 64 tokens, fp64 dot products. Every
+// K1b: c_t = cos(M, g_t) for a query-prep tile, fp64 dot products. Every
 // workgroup forms M = (1/C) sum_t g_t itself from the tile sums, in a fixed
 // order (a device-scope hand-off from one workgroup to the others would cost
 // an L2 write-back per workgroup on this chip, more than the repeated sum).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int kTokPerWave>
 __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
     const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ plan, int S, int Hkv,
     int64_t TC, const float* __restrict__ g, const double* __restrict__ gpart,
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
   double m[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) m[e] = Md[lane * EPL + e];
-  const int tw = (tile - qt_off[s]) * kQprepTokens + wave * kTokPerWave;
+  const int tw = (tile - qt_off[s]) * (kQprepWaves * kTokPerWave) + wave * kTokPerWave;
   float x[kTokPerWave][EPL];
 #pragma unroll
   for (int i = 0; i < kTokPerWave; ++i) {
@@ -674,33 +675,41 @@ hipError_t launch_qprep(const Problem& p, const void* q, char* ws, const Workspa
   const dim3 block(kQprepThreads);
   if (p.NQT == 0) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, p.cu_chunk, p.cu_hist, p.S,
-                       p.score_keys, plan, zero, n16);
+                       p.qtok, p.score_keys, plan, zero, n16);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
     dim3 grid((unsigned)p.NQT, (unsigned)p.Hkv);
-#define QUOKA_QPREP(T, D)                                                                     \
-  hipLaunchKernelGGL((qprep_g_kernel<T, D>), grid, block, 0, st, (const T*)q, p.cu_chunk,     \
+    const int tpw = p.qtok / kQprepWaves;  // tokens per wave: 4, 2 or 1
+#define QUOKA_QPREP1(T, D, TPW)                                                               \
+  hipLaunchKernelGGL((qprep_g_kernel<T, D, TPW>), grid, block, 0, st, (const T*)q, p.cu_chunk, \
                      p.cu_hist, p.S, p.Hq, p.Hkv, p.G, g, gpart, p.score_keys, plan, zero, n16)
+#define QUOKA_QPREP(T, D)                                                                     \
+  { if (tpw == 4) QUOKA_QPREP1(T, D, 4); else if (tpw == 2) QUOKA_QPREP1(T, D, 2);            \
+    else QUOKA_QPREP1(T, D, 1); }
     if (p.dtype == QUOKA_BF16) {
-      if (p.D == 128) QUOKA_QPREP(bf16, 128); else QUOKA_QPREP(bf16, 64);
+      if (p.D == 128) QUOKA_QPREP(bf16, 128) else QUOKA_QPREP(bf16, 64)
     } else {
-      if (p.D == 128) QUOKA_QPREP(float, 128); else QUOKA_QPREP(float, 64);
+      if (p.D == 128) QUOKA_QPREP(float, 128) else QUOKA_QPREP(float, 64)
     }
 #undef QUOKA_QPREP
+#undef QUOKA_QPREP1
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // the select keeps every token of a chunk that has at most q_budget of them,
     // whatever their cosines; the mean-query baseline does not subselect at all
     const bool need_cos =
         p.variant != QUOKA_VARIANT_MEAN_QUERY && (want_cos || p.maxC > p.q_budget);
-    if (!need_cos) {
-    } else if (p.D == 128)
-      hipLaunchKernelGGL((qprep_cos_kernel<128>), grid, block, 0, st, p.cu_chunk, plan, p.S,
-                         p.Hkv, p.TC, g, gpart, qcos);
-    else
-      hipLaunchKernelGGL((qprep_cos_kernel<64>), grid, block, 0, st, p.cu_chunk, plan, p.S,
-                         p.Hkv, p.TC, g, gpart, qcos);
+#define QUOKA_QCOS(D, TPW)                                                                    \
+  hipLaunchKernelGGL((qprep_cos_kernel<D, TPW>), grid, block, 0, st, p.cu_chunk, plan, p.S,   \
+                     p.Hkv, p.TC, g, gpart, qcos)
+#define QUOKA_QCOS_D(D)                                                                       \
+  { if (tpw == 4) QUOKA_QCOS(D, 4); else if (tpw == 2) QUOKA_QCOS(D, 2); else QUOKA_QCOS(D, 1); }
+    if (need_cos) {
+      if (p.D == 128) QUOKA_QCOS_D(128) else QUOKA_QCOS_D(64)
+    }
+#undef QUOKA_QCOS_D
+#undef QUOKA_QCOS
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
