@@ -281,7 +281,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first; the first few tens of steps after start run "
+                         "slower (the clocks settle), so the default is 50")
     ap.add_argument("--config", default="long", choices=sorted(DESCR))
     ap.add_argument("--input-sets", type=int, default=0,
                     help="rotated copies of the inputs cycled through (default: enough for "
