@@ -542,12 +542,20 @@ AttnPlan attn_plan(const Problem& p) {
   const int64_t rows = (int64_t)p.maxC * p.G;
   const int64_t n128 = (rows + 127) / 128;
   const int64_t grid4 = n128 * p.Hkv * p.S;  // four-wave workgroups the shape needs
-  // eight waves on 256 contiguous rows when that still leaves two workgroups
-  // per CU; eight waves on a heavy and a light 128-row tile when four-wave
-  // workgroups would fill the chip exactly once (then pairing balances the
-  // CUs and shares the K/V loads); else four waves
-  const bool wide = (rows + 255) / 256 * p.Hkv * p.S >= kAttnWideMinBlocks;
-  const int pair = (!wide && grid4 > 256 && grid4 <= kAttnResident4) ? 1 : 0;
+  // Eight waves on a heavy and a light 128-row tile (the paired order: every
+  // workgroup gets the same work and its halves share the K/V loads) when
+  // four-wave workgroups would fill the chip exactly once, or when there are
+  // enough for eight-wave workgroups and the chunk spans at most half as many
+  // key tiles as the kept history (the light half then idles only briefly:
+  // ragged layer 112 -> 107 us); eight waves on 256 contiguous rows when
+  // there are enough for them and the chunk is longer (long layer: the
+  // paired order's light halves idled, 406 -> 415 us); else four waves.
+  const bool many = (rows + 255) / 256 * p.Hkv * p.S >= kAttnWideMinBlocks;
+  const int64_t hist_tiles = (p.kv_budget + 63) / 64, chunk_tiles = (p.maxC + 63) / 64;
+  const bool short_chunk = chunk_tiles * 2 <= hist_tiles;
+  const bool wide = many && !short_chunk;
+  const int pair =
+      ((!many && grid4 > 256 && grid4 <= kAttnResident4) || (many && short_chunk)) ? 1 : 0;
   const int nw = (wide || pair) ? 8 : 4;
   const int ntile = (int)(nw == 8 ? (n128 + 1) / 2 : n128);
   // at most half the CUs busy (few rows: short chunks, decode): split each

@@ -193,6 +193,10 @@ ORDER_CASES = {
     "split6_chunk": ([(300, 100)], 8, 2, 128, "bf16", 8, 64),
     # GQA 7: 128-row tiles cut through a token's heads (paired order, 66 tiles)
     "pair_g7": ([(1200, 3000)], 28, 4, 128, "bf16", 16, 512),
+    # enough tiles for eight-wave workgroups, but a chunk of at most half the
+    # kept history's key tiles: the paired order (15 tiles per problem, so one
+    # middle tile without a partner), over 8 sequences
+    "pair_short_chunk": ([(480, 5000)] * 8, 32, 8, 128, "bf16", 8, 1024),
     # one query head per KV head in the wide order, chunks of different lengths
     "wide_g1": ([(4096, 300), (3000, 900)] * 4, 8, 8, 128, "bf16", 8, 128),
 }
