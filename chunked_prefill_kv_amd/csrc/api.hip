@@ -148,6 +148,20 @@ quoka_status make_problem(const quoka_shape* sh, int q_budget, int kv_budget, Pr
   // sequences).
   p->score_keys = kScoreKeysMin;
   p->NSB = scorer_tiles(*sh, p->score_keys);
+  // With at most 32 kept rows (two 16-row blocks) a key block costs few
+  // products and the scorer streams: tiles of 512 keys or more, the smallest
+  // that gives at most two rounds (narrow layer 22.0 -> 20.3 us at 512 keys;
+  // decode 59.3 -> 56.8 us at 1024 instead of 2048).
+  if (std::min<int64_t>(q_budget, p->maxC) <= 32) {
+    for (int k = 2 * kScoreKeysMin; k <= kScoreKeysMax; k *= 2) {
+      const int64_t n = scorer_tiles(*sh, k);
+      if (n * p->Hkv <= 2 * kScoreMaxBlocks) {
+        p->score_keys = k;
+        p->NSB = n;
+        break;
+      }
+    }
+  }
   if (p->NSB * p->Hkv > 2 * kScoreMaxBlocks) {
     while (p->score_keys < kScoreKeysMax && p->NSB * p->Hkv > kScoreMaxBlocks) {
       const int64_t n = scorer_tiles(*sh, p->score_keys * 2);
