@@ -75,6 +75,19 @@ __device__ __forceinline__ void load4(const T* __restrict__ p, float (&x)[4]) {
   }
 }
 
+// 1/sqrt(x) in fp64 for x > 0: the hardware estimate refined by two
+// Newton-Raphson steps r <- r (3 - x r^2) / 2, each of which squares the
+// estimate's relative error, so the result is the fp64 value to a few units
+// in the last place (about half the cost of a correctly rounded sqrt and a
+// division).
+__device__ __forceinline__ double rsqrt_f64(double x) {
+  double r = __builtin_amdgcn_rsq(x);
+  const double hx = -0.5 * x;
+  r = r * fma(hx, r * r, 1.5);
+  r = r * fma(hx, r * r, 1.5);
+  return r;
+}
+
 // Sum over the RL lanes of one head row (aligned groups of RL = 16 or 32).
 template <int RL>
 __device__ __forceinline__ double head_row_sum(double v) {
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
 #pragma unroll
       for (int e = 0; e < EPL; ++e) ss = fma((double)x[i][e], (double)x[i][e], ss);
       ss = head_row_sum<RL>(ss);
-      const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+      const double inv = ss > 0.0 ? rsqrt_f64(ss) : 0.0;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[i][e] = fma((double)x[i][e], inv, acc[i][e]);
     }
@@ -399,7 +412,7 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
   double msq = 0.0;
 #pragma unroll
   for (int w = 0; w < kQprepWaves; ++w) msq += red[w];
-  const double mnorm = sqrt(msq);
+  const double minv = msq > 0.0 ? rsqrt_f64(msq) : 0.0;  // 1 / |M|
 
   constexpr int EPL = D / 64;
   double m[EPL];
@@ -427,8 +440,8 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_cos_kernel(
     gg = wave_sum(gg);
     const int t = tw + i;
     if (lane == 0 && t < C) {
-      const double den = mnorm * sqrt(gg);
-      qcos[(int64_t)h * TC + c_off + t] = den > 0.0 ? (float)(dot / den) : 0.f;
+      const double ginv = gg > 0.0 ? rsqrt_f64(gg) : 0.0;  // 1 / |g_t|
+      qcos[(int64_t)h * TC + c_off + t] = (float)(dot * ginv * minv);
     }
   }
 }
