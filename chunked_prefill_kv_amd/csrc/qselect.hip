@@ -226,13 +226,40 @@ __global__ __launch_bounds__(kQprepThreads) void qprep_g_kernel(
 // keys (tokens surely in, then the band by fp64 value, then the rest) kept
 // in kbuf [C].
 // ---------------------------------------------------------------------------
+// Exclusive prefix sum of cnt over the block, and the block's maximum of mx
+// and minimum of mn, in one exchange through LDS.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_max_min(uint32_t cnt, uint32_t& mx, uint32_t& mn,
+                                                       RadixScratch<NT>& rs) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t x = wave_inclusive_scan(cnt);
+  const uint32_t wmx = ~wave_min(~mx), wmn = wave_min(mn);
+  if (lane == 63) rs.wsum[w] = x;
+  if (lane == 0) {
+    rs.wand[w] = wmx;
+    rs.wor[w] = wmn;
+  }
+  __syncthreads();
+  uint32_t add = 0, bmx = 0u, bmn = ~0u;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    if (i < w) add += rs.wsum[i];
+    bmx = max(bmx, (uint32_t)rs.wand[i]);
+    bmn = min(bmn, (uint32_t)rs.wor[i]);
+  }
+  __syncthreads();
+  mx = bmx;
+  mn = bmn;
+  return x - cnt + add;
+}
+
 template <int NT, typename ExactFn>
 __device__ int select_tokens(int C, int q_budget, const float* __restrict__ src, float* cs,
                              RadixScratch<NT>& rs, float err, uint64_t* __restrict__ kbuf,
                              ExactFn exact_cos, int32_t* __restrict__ out, int32_t* kept) {
   const int n = min(q_budget, C);
   if (C <= kQselCap && src != cs) {
-    block_copy<NT, 4>(cs, src, C);
+    block_copy<NT, 8>(cs, src, C);  // up to 8 NT cosines in one round of loads
     src = cs;
   }
   __syncthreads();
@@ -241,18 +268,28 @@ __device__ int select_tokens(int C, int q_budget, const float* __restrict__ src,
   };
   uint64_t prefix = ~0ull, mask = ~0ull;  // keep everything when n == C
   bool use_k = false;
-  if (n < C) {
-    radix_select<false, NT>(approx_key, C, n, rs, prefix, mask);
-    // cn, the n-th lowest fp32 cosine: when every token left out lies more
-    // than 2 err above it, the fp32 selection is the fp64 one
-    uint32_t kn = 0u, kout = ~0u;
-    for (int t = threadIdx.x; t < C; t += NT) {
-      const uint64_t k = approx_key(t);
-      if (radix_taken<false>(k, prefix, mask)) kn = max(kn, (uint32_t)(k >> 32));
-      else kout = min(kout, (uint32_t)(k >> 32));
+  if (n < C) radix_select<false, NT>(approx_key, C, n, rs, prefix, mask);
+  auto key_of = [&](int t) -> uint64_t { return use_k ? kbuf[t] : approx_key(t); };
+
+  // ascending compaction of the kept tokens (each thread a contiguous range);
+  // the same pass finds cn, the n-th lowest fp32 cosine, and the lowest one
+  // left out
+  const int per = (C + NT - 1) / NT;
+  const int b0 = threadIdx.x * per, b1 = min(C, b0 + per);
+  uint32_t cnt = 0, kn = 0u, kout = ~0u;
+  for (int t = b0; t < b1; ++t) {
+    const uint64_t k = approx_key(t);
+    if (radix_taken<false>(k, prefix, mask)) {
+      ++cnt;
+      kn = max(kn, (uint32_t)(k >> 32));
+    } else {
+      kout = min(kout, (uint32_t)(k >> 32));
     }
-    kn = block_max<NT>(kn, rs);
-    kout = block_min<NT>(kout, rs);
+  }
+  uint32_t pos = block_scan_max_min<NT>(cnt, kn, kout, rs);
+  if (n < C) {
+    // when every token left out lies more than 2 err above cn, the fp32
+    // selection is the fp64 one; else the band within 2 err of cn is re-ranked
     const double cn = (double)float_from_order_key(kn);
     const double lo = cn - 2.0 * (double)err, hi = cn + 2.0 * (double)err;
     if ((double)float_from_order_key(kout) <= hi) {
@@ -273,16 +310,11 @@ __device__ int select_tokens(int C, int q_budget, const float* __restrict__ src,
       __syncthreads();
       radix_select<false, NT>([&](int t) { return kbuf[t]; }, C, n, rs, prefix, mask);
       use_k = true;
+      cnt = 0;
+      for (int t = b0; t < b1; ++t) cnt += radix_taken<false>(key_of(t), prefix, mask);
+      pos = block_exclusive_scan<NT>(cnt, rs);
     }
   }
-  auto key_of = [&](int t) -> uint64_t { return use_k ? kbuf[t] : approx_key(t); };
-
-  // ascending compaction of the kept tokens
-  const int per = (C + NT - 1) / NT;
-  const int b0 = threadIdx.x * per, b1 = min(C, b0 + per);
-  uint32_t cnt = 0;
-  for (int t = b0; t < b1; ++t) cnt += radix_taken<false>(key_of(t), prefix, mask);
-  uint32_t pos = block_exclusive_scan<NT>(cnt, rs);
   for (int t = b0; t < b1; ++t) {
     if (radix_taken<false>(key_of(t), prefix, mask)) {
       out[pos] = t;
