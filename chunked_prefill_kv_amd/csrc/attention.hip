@@ -248,9 +248,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   // Direct loads: a wave instruction writes 1 KB of LDS (lane l at +16 l),
   // i.e. RPP rows of CPR 16-byte chunks; lane l of piece P takes row
   // P*RPP + l/CPR and fetches the chunk that belongs in slot l%CPR: chunk
-  // slot ^ (row & 7) for K, slot ^ 2(row & 3) for V (the swizzles that keep
-  // the K row reads and the V transpose reads free of bank conflicts).
+  // slot ^ kswz(row) for K, slot ^ vswz(row) for V. LDS serves 64 4-byte
+  // banks; a 16-byte read takes 16 lanes at a time and an 8-byte transposing
+  // read 32, and a group whose lanes share a bank pays an extra cycle (both
+  // measured on the chip: with slot ^ (row & 7) every K read of 16 rows paid
+  // 4 extra cycles, with slot ^ 2(row & 3) every V read of 4 rows x 4 chunks
+  // 2). The swizzles spread the 16 rows of a K read over all 64 banks and
+  // the 4 x 4 chunks of a V read likewise.
   constexpr int CPR = D / 8, RPP = 64 / CPR, NP = KT / RPP / NW;  // pieces per wave per tensor
+  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 2 * (r & 3); };
   static_assert(NP >= 1 && KT % (RPP * NW) == 0, "tile must split into whole pieces per wave");
   int prow[NP];
   uint32_t kcol[NP], vcol[NP];
@@ -258,8 +265,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   for (int u = 0; u < NP; ++u) {
     const int r = (wave * NP + u) * RPP + lane / CPR, sl = lane % CPR;
     prow[u] = r;
-    kcol[u] = (uint32_t)(sl ^ (r & 7)) * 16u;
-    vcol[u] = (uint32_t)(sl ^ (2 * (r & 3))) * 16u;
+    kcol[u] = (uint32_t)(sl ^ kswz(r)) * 16u;
+    vcol[u] = (uint32_t)(sl ^ vswz(r)) * 16u;
   }
   // kIdx: history row indices of the next tile to load, fetched one tile
   // ahead so that a row load never waits for its own index load
@@ -314,17 +321,19 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   // lane-constant parts of the LDS read addresses
   const int g16 = lane >> 4, j16 = lane & 15;
   // K operand of d-step ds: row sb*32 + col, chunk 2 ds + hi stored at
-  // chunk (2 ds + hi) ^ (col & 7); ds and ds + 4 differ by 8 chunks
-  int koff[4];
+  // slot (2 ds + hi) ^ kswz(col) (sb*32 leaves kswz unchanged)
+  int koff[NDS];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) koff[j] = col * D + (((2 * j) ^ (hi ^ (col & 7))) << 3);
-  // V transpose reads: row hi*4 + j16/4 (+ tile offsets, all multiples of 4),
-  // columns db*32 + (g16&1)*16 + 4(j16&3); chunk c sits at c ^ 2(j16/4)
+  for (int ds = 0; ds < NDS; ++ds) koff[ds] = col * D + (((2 * ds + hi) ^ kswz(col)) << 3);
+  // V transpose reads: row hi*4 + j16/4 (+ tile offsets, all multiples of 8,
+  // which leave vswz unchanged), columns db*32 + (g16&1)*16 + 4(j16&3);
+  // chunk c sits at c ^ vswz(row)
   int voff[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int c = db * 4 + (g16 & 1) * 2 + ((j16 & 3) >> 1);
-    voff[db] = (hi * 4 + (j16 >> 2)) * D + ((c ^ (2 * (j16 >> 2))) << 3) + 4 * (j16 & 1);
+    const int row = hi * 4 + (j16 >> 2);
+    voff[db] = row * D + ((c ^ vswz(row)) << 3) + 4 * (j16 & 1);
   }
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds)
-        ka[sb][ds] = *(const bf16x8*)(ks + sb * 32 * D + koff[ds & 3] + (ds >> 2) * 64);
+        ka[sb][ds] = *(const bf16x8*)(ks + sb * 32 * D + koff[ds]);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
