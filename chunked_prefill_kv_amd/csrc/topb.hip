@@ -159,10 +159,18 @@ __device__ void exact_keys(const TopbArgs& a, int s, int h, const int* __restric
   const int GH = a.variant == QUOKA_VARIANT_PER_HEAD ? a.G : 1;
   const int nrows = C == 0 ? 0 : one ? 1 : min(a.q_budget, C);
   const int32_t* kept = a.qidx + (int64_t)prob * a.q_budget;
+  // LDS slot of 16-byte piece c of batch key i's row: bf16 rows are stored
+  // with their pieces permuted (c ^ (i & 15) for d = 128, c ^ ((i >> 1) & 7)
+  // for d = 64) so that the screen's B-operand reads, one piece of 16 rows
+  // per 16 lanes, hit distinct banks
+  auto kslot = [](int i, int c) -> int {
+    if constexpr (sizeof(T) != 2) return c;
+    else return c ^ (D == 128 ? (i & 15) : ((i >> 1) & 7));
+  };
   // element e of the LDS row of batch key i
   auto kel = [&](int i, int e) -> double {
-    const T* row = (const T*)&xs.krows[i][0];
-    return (double)to_f32(row[e]);
+    const T* row = (const T*)&xs.krows[i][kslot(i, e / EPC)];
+    return (double)to_f32(row[e % EPC]);
   };
   if (one && nrows > 0)
     for (int d = threadIdx.x; d < D; d += 256) xs.row0[d] = a.row0[(int64_t)prob * D + d];
@@ -180,7 +188,7 @@ __device__ void exact_keys(const TopbArgs& a, int s, int h, const int* __restric
     for (int c = threadIdx.x; c < kExactBatch * CPR; c += 256) {
       const int i = c / CPR, pc = c - i * CPR;
       const T* row = kh + ((int64_t)(h_off + xs.kidx[i]) * a.Hkv + h) * D;
-      xs.krows[i][pc] = *(const uint4*)(row + pc * EPC);
+      xs.krows[i][kslot(i, pc)] = *(const uint4*)(row + pc * EPC);
     }
     __syncthreads();
     // |k|^2 in fp64 (exact products of bf16 values), quad i for key i
@@ -217,7 +225,7 @@ __device__ void exact_keys(const TopbArgs& a, int s, int h, const int* __restric
             bf16x8 kb[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-              kb[c] = __builtin_bit_cast(bf16x8, xs.krows[c * 16 + (lane & 15)][ds * 4 + (lane >> 4)]);
+              kb[c] = __builtin_bit_cast(bf16x8, xs.krows[c * 16 + (lane & 15)][kslot(c * 16 + (lane & 15), ds * 4 + (lane >> 4))]);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               if (wave + 4 * j < nqb) {
@@ -289,7 +297,11 @@ __device__ void exact_keys(const TopbArgs& a, int s, int h, const int* __restric
           const int i = (int)(pr >> 8), r = (int)(pr & 255u);
           Raw8<T> kr[OL];  // this lane's slice of the key, in its storage type
 #pragma unroll
-          for (int u = 0; u < OL; ++u) kr[u].load((const T*)&xs.krows[i][0] + ol * OE + u * 8);
+          for (int u = 0; u < OL; ++u) {
+            // 8 elements: one piece (bf16), or two consecutive ones (fp32, unpermuted)
+            const int e0 = ol * OE + u * 8;
+            kr[u].load((const T*)&xs.krows[i][kslot(i, e0 / EPC)] + e0 % EPC);
+          }
           double dot = 0.0;
           if (one) {
 #pragma unroll
