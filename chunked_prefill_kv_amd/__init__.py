@@ -20,7 +20,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libquoka.so")
 
-QUOKA_OK, QUOKA_EINVAL, QUOKA_EUNSUPPORTED, QUOKA_EWORKSPACE, QUOKA_EHIP = range(5)
+QUOKA_OK, QUOKA_EINVAL, QUOKA_EUNSUPPORTED, QUOKA_EWORKSPACE, QUOKA_EHIP, QUOKA_ECHECK = range(6)
 QUOKA_F32, QUOKA_BF16 = 0, 1
 MAX_Q_BUDGET = 128
 # quoka_variant: QUOKA and the baseline selections the pages compare it with
@@ -28,7 +28,7 @@ VARIANTS = {"quoka": 0, "dot": 1, "mean_queries": 2, "mean_query": 3, "per_head"
             "global": 5}
 
 SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
-           "quoka_select_variant", "quoka_gather",
+           "quoka_select_variant", "quoka_gather", "quoka_check_selection",
            "quoka_attn_workspace_bytes", "quoka_chunk_attn",
            "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prefill_chunk_static",
            "quoka_prompt_workspace_bytes",
@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH):
     lib.quoka_select_variant.argtypes = [sp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.quoka_select_profiled.argtypes = [sp, vp, vp, i32, i32, vp, vp, sz, vp, vp]
     lib.quoka_gather.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp]
+    lib.quoka_check_selection.argtypes = [sp, vp, i32, vp]
     lib.quoka_attn_workspace_bytes.argtypes = [sp, i32, P(sz)]
     lib.quoka_chunk_attn.argtypes = [sp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.quoka_chunk_attn_gather.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
@@ -100,7 +101,7 @@ def load_library(path: str = LIB_PATH):
     lib.quoka_prefill_prompt.argtypes = [pp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp,
                                          sz, vp]
     for f in ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
-              "quoka_select_variant", "quoka_gather", "quoka_chunk_attn",
+              "quoka_select_variant", "quoka_gather", "quoka_check_selection", "quoka_chunk_attn",
               "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prefill_chunk_static",
               "quoka_prompt_workspace_bytes", "quoka_prefill_prompt"):
         getattr(lib, f).restype = ctypes.c_int
@@ -293,6 +294,16 @@ def gather(shape: Shape, k_hist, v_hist, sel_idx, kv_budget: int, *, k_sel=None,
                             kv_budget, _ptr(k_sel), _ptr(v_sel), _stream(shape.device)),
            "quoka_gather")
     return k_sel, v_sel
+
+
+def check_selection(shape: Shape, sel_idx, kv_budget: int):
+    """Raises QuokaError (status QUOKA_ECHECK) unless every (s, h) of sel_idx
+    holds B_eff strictly ascending history positions followed by -1 padding."""
+    lib = load_library()
+    shape._check_tensor(sel_idx, "sel_idx", (shape.num_seqs, shape.num_kv_heads, kv_budget),
+                        torch.int32)
+    _check(lib.quoka_check_selection(ctypes.byref(shape.c), _ptr(sel_idx), kv_budget,
+                                     _stream(shape.device)), "quoka_check_selection")
 
 
 def chunk_attn(shape: Shape, q, k_sel, v_sel, kv_budget: int, k_chunk, v_chunk,

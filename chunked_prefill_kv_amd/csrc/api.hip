@@ -9,14 +9,15 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "common.h"
+#include "debug.h"
 #include "internal.h"
 #include "quoka.h"
 
 namespace quoka {
-namespace {
 
 thread_local char g_err[512] = "";
 
@@ -28,13 +29,31 @@ quoka_status fail(quoka_status st, const char* fmt, ...) {
   return st;
 }
 
+namespace {
+
 bool sync_mode() {
   static const bool on = [] {
     const char* v = std::getenv("QUOKA_SYNC");
     return v && v[0] && std::strcmp(v, "0") != 0;
   }();
-  return on;
+  return on || debug_mode();
 }
+
+// QUOKA_DEBUG: the arguments' checks, run before a call's first compute
+// kernel (debug.hip); nothing when the mode is off.
+quoka_status debug_inputs(const Problem& p, std::initializer_list<DebugItem> items,
+                          hipStream_t st) {
+  if (!debug_mode()) return QUOKA_OK;
+  const quoka_status rc = debug_offsets(p);
+  if (rc != QUOKA_OK) return rc;
+  return debug_run(p, items.begin(), (int)items.size(), st);
+}
+
+// element counts of the arguments
+int64_t n_q(const Problem& p) { return p.TC * p.Hq * p.D; }
+int64_t n_hist(const Problem& p) { return p.TL * p.Hkv * p.D; }
+int64_t n_chunk(const Problem& p) { return p.TC * p.Hkv * p.D; }
+int64_t n_sel(const Problem& p) { return (int64_t)p.S * p.Hkv * p.kv_budget; }
 
 quoka_status hip_check(hipError_t e, const char* what, hipStream_t st) {
   if (e == hipSuccess && sync_mode()) e = hipStreamSynchronize(st);
@@ -288,7 +307,12 @@ quoka_status run_select(const Problem& p, const Workspace& w, const void* q, con
   if ((rc = mark(2))) return rc;
   if ((rc = hip_check(launch_topb(p, q, k_hist, qidx, ws, w, scores, sel_idx, st), "topb", st)))
     return rc;
-  return mark(3);
+  if ((rc = mark(3))) return rc;
+  if (debug_mode()) {
+    const DebugItem it{sel_idx, n_sel(p), kDebugIdxSelection, kDbgSelOut};
+    return debug_run(p, &it, 1, st);
+  }
+  return QUOKA_OK;
 }
 
 #define QUOKA_NEED(ptr, total)                                                          \
@@ -364,6 +388,9 @@ quoka_status quoka_select(const quoka_shape* shape, const void* q, const void* k
   const Workspace w = workspace_layout(p);
   if (ws_bytes < w.total)
     return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  if ((rc = debug_inputs(p, {{q, n_q(p), kDebugRowsAll, kDbgQ},
+                             {k_hist, n_hist(p), kDebugRowsAll, kDbgKHist}}, stream)))
+    return rc;
   return run_select(p, w, q, k_hist, sel_idx, q_idx_opt, qcos_opt, scores_opt, (char*)ws,
                     stream);
 }
@@ -387,6 +414,9 @@ quoka_status quoka_select_profiled(const quoka_shape* shape, const void* q, cons
   const Workspace w = workspace_layout(p);
   if (ws_bytes < w.total)
     return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  if ((rc = debug_inputs(p, {{q, n_q(p), kDebugRowsAll, kDbgQ},
+                             {k_hist, n_hist(p), kDebugRowsAll, kDbgKHist}}, stream)))
+    return rc;
   return run_select(p, w, q, k_hist, sel_idx, nullptr, nullptr, nullptr, (char*)ws, stream,
                     events);
 }
@@ -409,6 +439,9 @@ quoka_status quoka_select_variant(const quoka_shape* shape, int32_t variant, con
   const Workspace w = workspace_layout(p);
   if (ws_bytes < w.total)
     return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
+  if ((rc = debug_inputs(p, {{q, n_q(p), kDebugRowsAll, kDbgQ},
+                             {k_hist, n_hist(p), kDebugRowsAll, kDbgKHist}}, stream)))
+    return rc;
   return run_select(p, w, q, k_hist, sel_idx, q_idx_opt, qcos_opt, scores_opt, (char*)ws,
                     stream);
 }
@@ -425,8 +458,23 @@ quoka_status quoka_gather(const quoka_shape* shape, const void* k_hist, const vo
   QUOKA_NEED(sel_idx, 1);
   QUOKA_NEED(k_sel, 1);
   QUOKA_NEED(v_sel, 1);
+  if ((rc = debug_inputs(p, {{k_hist, n_hist(p), kDebugRowsAll, kDbgKHist},
+                             {v_hist, n_hist(p), kDebugRowsAll, kDbgVHist},
+                             {sel_idx, n_sel(p), kDebugIdxInput, kDbgSelIn}}, stream)))
+    return rc;
   return hip_check(launch_gather(p, k_hist, v_hist, sel_idx, k_sel, v_sel, stream), "gather",
                    stream);
+}
+
+quoka_status quoka_check_selection(const quoka_shape* shape, const int32_t* sel_idx,
+                                   int32_t kv_budget, hipStream_t stream) {
+  g_err[0] = 0;
+  Problem p;
+  quoka_status rc = make_problem(shape, 1, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  QUOKA_NEED(sel_idx, 1);
+  const DebugItem it{sel_idx, n_sel(p), kDebugIdxSelection, kDbgSelOut};
+  return debug_run(p, &it, 1, stream);
 }
 
 quoka_status quoka_attn_workspace_bytes(const quoka_shape* shape, int32_t kv_budget,
@@ -456,6 +504,12 @@ quoka_status quoka_chunk_attn(const quoka_shape* shape, const void* q, const voi
   QUOKA_NEED(out, p.TC);
   if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
   if ((rc = attn_ws_check(p, ws, ws_bytes))) return rc;
+  if ((rc = debug_inputs(p, {{q, n_q(p), kDebugRowsAll, kDbgQ},
+                             {k_sel, n_sel(p) * p.D, kDebugRowsSel, kDbgKSel},
+                             {v_sel, n_sel(p) * p.D, kDebugRowsSel, kDbgVSel},
+                             {k_chunk, n_chunk(p), kDebugRowsAll, kDbgKChunk},
+                             {v_chunk, n_chunk(p), kDebugRowsAll, kDbgVChunk}}, stream)))
+    return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
   return hip_check(
       launch_attention(p, q, k_sel, v_sel, nullptr, k_chunk, v_chunk, scale, out, ws, stream),
@@ -480,6 +534,13 @@ quoka_status quoka_chunk_attn_gather(const quoka_shape* shape, const void* q, co
   QUOKA_NEED(out, p.TC);
   if (!std::isfinite(softmax_scale)) return fail(QUOKA_EINVAL, "softmax_scale is not finite");
   if ((rc = attn_ws_check(p, ws, ws_bytes))) return rc;
+  if ((rc = debug_inputs(p, {{q, n_q(p), kDebugRowsAll, kDbgQ},
+                             {k_hist, n_hist(p), kDebugRowsAll, kDbgKHist},
+                             {v_hist, n_hist(p), kDebugRowsAll, kDbgVHist},
+                             {sel_idx, n_sel(p), kDebugIdxInput, kDbgSelIn},
+                             {k_chunk, n_chunk(p), kDebugRowsAll, kDbgKChunk},
+                             {v_chunk, n_chunk(p), kDebugRowsAll, kDbgVChunk}}, stream)))
+    return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
   return hip_check(
       launch_attention(p, q, k_hist, v_hist, sel_idx, k_chunk, v_chunk, scale, out, ws, stream),
@@ -509,6 +570,12 @@ quoka_status quoka_prefill_chunk(const quoka_shape* shape, const void* q, const 
     return fail(QUOKA_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, w.total);
   char* base = (char*)ws;
   int32_t* sel = sel_idx_opt ? sel_idx_opt : (int32_t*)(base + w.selidx);
+  if ((rc = debug_inputs(p, {{q, n_q(p), kDebugRowsAll, kDbgQ},
+                             {k_hist, n_hist(p), kDebugRowsAll, kDbgKHist},
+                             {v_hist, n_hist(p), kDebugRowsAll, kDbgVHist},
+                             {k_chunk, n_chunk(p), kDebugRowsAll, kDbgKChunk},
+                             {v_chunk, n_chunk(p), kDebugRowsAll, kDbgVChunk}}, stream)))
+    return rc;
   rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
   if (rc != QUOKA_OK) return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
@@ -543,6 +610,12 @@ quoka_status quoka_prefill_chunk_static(const quoka_shape* shape, const void* q,
   char* base = nullptr;
   if ((rc = static_scratch(&base))) return rc;
   int32_t* sel = sel_idx_opt ? sel_idx_opt : (int32_t*)(base + w.selidx);
+  if ((rc = debug_inputs(p, {{q, n_q(p), kDebugRowsAll, kDbgQ},
+                             {k_hist, n_hist(p), kDebugRowsAll, kDbgKHist},
+                             {v_hist, n_hist(p), kDebugRowsAll, kDbgVHist},
+                             {k_chunk, n_chunk(p), kDebugRowsAll, kDbgKChunk},
+                             {v_chunk, n_chunk(p), kDebugRowsAll, kDbgVChunk}}, stream)))
+    return rc;
   rc = run_select(p, w, q, k_hist, sel, nullptr, nullptr, nullptr, base, stream);
   if (rc != QUOKA_OK) return rc;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.D);
@@ -646,6 +719,15 @@ quoka_status quoka_prefill_prompt(const quoka_prompt* prompt, const void* q, con
     if ((rc = make_problem(&sh, q_budget, kv_budget, &p))) return rc;
     const Workspace w = workspace_layout(p);
     int32_t* sel = sel_idx_opt ? sel_idx_opt + (size_t)i * sel_chunk : (int32_t*)(base + lay.sel);
+    if (debug_mode()) {
+      // the whole prompt's rows once, then every chunk's device offsets
+      const int64_t nq = (int64_t)T * p.Hq * p.D, nk = (int64_t)T * p.Hkv * p.D;
+      if (i == 0 && (rc = debug_inputs(p, {{q, nq, kDebugRowsAll, kDbgQ},
+                                           {k, nk, kDebugRowsAll, kDbgK},
+                                           {v, nk, kDebugRowsAll, kDbgV}}, stream)))
+        return rc;
+      if ((rc = debug_offsets(p))) return rc;
+    }
     const char* qi = (const char*)q + (size_t)a * qrow;
     rc = run_select(p, w, qi, k, sel, nullptr, nullptr, nullptr, base + lay.chunk_ws, stream);
     if (rc != QUOKA_OK) return rc;
@@ -667,6 +749,7 @@ const char* quoka_strerror(quoka_status status) {
     case QUOKA_EUNSUPPORTED: return "unsupported configuration";
     case QUOKA_EWORKSPACE: return "workspace missing or too small";
     case QUOKA_EHIP: return "HIP error";
+    case QUOKA_ECHECK: return "result failed its check";
   }
   return "unknown status";
 }

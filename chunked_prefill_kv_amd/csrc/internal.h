@@ -109,6 +109,9 @@ ScoreBounds score_bounds(const Problem& p);
 
 Workspace workspace_layout(const Problem& p);
 
+// Records the message quoka_last_error() returns on this thread; returns st.
+quoka_status fail(quoka_status st, const char* fmt, ...);
+
 // Launchers (enqueue only; return hipGetLastError()).
 // Raise the dynamic-LDS limit of the scorer kernels (they hold the kept
 // queries and a score histogram on chip).

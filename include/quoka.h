@@ -45,6 +45,22 @@
  * returns QUOKA_EHIP. Device faults surface asynchronously, as with any HIP
  * call; set the environment variable QUOKA_SYNC=1 to synchronize the stream
  * after every launch and report them as QUOKA_EHIP.
+ *
+ * Debug mode: with the environment variable QUOKA_DEBUG set (to anything but
+ * "0"; read on every call) each entry point also checks on the device, before
+ * its first compute kernel, what the host cannot see, and synchronizes the
+ * stream after every launch:
+ *   - the device offset arrays hold the host copies' values;
+ *   - every element of q, k_hist, v_hist, k_chunk, v_chunk it reads is finite
+ *     (k_sel / v_sel: the rows below B_eff, the only ones read);
+ *   - a sel_idx it takes as input holds -1 or positions in [0, L_s) (stricter
+ *     than quoka_chunk_attn_gather's own contract, which reads any other value
+ *     as a zero row: in debug mode such a value is reported);
+ * any of these fails with QUOKA_EINVAL and a message naming the argument and
+ * the first offending element. A sel_idx the call writes is then checked as
+ * quoka_check_selection does (QUOKA_ECHECK). The checks scan every input, so
+ * debug mode is for finding a caller's or the library's mistake, not for
+ * timing; calls in debug mode on one device are serialized.
  */
 #ifndef QUOKA_H
 #define QUOKA_H
@@ -63,7 +79,9 @@ typedef enum quoka_status {
   QUOKA_EINVAL = 1,        /* a null pointer, negative size or inconsistent offsets */
   QUOKA_EUNSUPPORTED = 2,  /* well-formed but outside what is built (head_dim, budget) */
   QUOKA_EWORKSPACE = 3,    /* workspace null or smaller than quoka_workspace_bytes() */
-  QUOKA_EHIP = 4           /* a HIP launch or query failed */
+  QUOKA_EHIP = 4,          /* a HIP launch or query failed */
+  QUOKA_ECHECK = 5         /* a result failed its check (QUOKA_DEBUG mode,
+                              quoka_check_selection) */
 } quoka_status;
 
 typedef enum quoka_dtype {
@@ -186,6 +204,17 @@ quoka_status quoka_gather(const quoka_shape* shape, const void* k_hist,
                           const void* v_hist, const int32_t* sel_idx,
                           int32_t kv_budget, void* k_sel, void* v_sel,
                           hipStream_t stream);
+
+/* Checks a kept-index array against the selection's layout: for every
+ * (s, h), entries b < B_eff = min(kv_budget, L_s) are strictly ascending
+ * positions in [0, L_s) and entries from B_eff on are -1 (the layout every
+ * quoka_select* call writes: "QUOKA Explained", "From scores to a smaller KV
+ * set", the kept set is B_eff distinct history keys). Reads sel_idx
+ * [S, H_kv, kv_budget] on the stream and waits for the result: QUOKA_OK, or
+ * QUOKA_ECHECK with quoka_last_error() naming the first offending (s, h, b).
+ * Allocates nothing; calls on one device are serialized. */
+quoka_status quoka_check_selection(const quoka_shape* shape, const int32_t* sel_idx,
+                                   int32_t kv_budget, hipStream_t stream);
 
 /* Bytes of device workspace quoka_chunk_attn / quoka_chunk_attn_gather need
  * for this shape (written to *bytes). Shapes whose bf16 attention fills at

@@ -79,6 +79,22 @@ def test_workspace_validation(lib, kw, qb, kvb, code):
     assert lib.quoka_strerror(code).decode()
 
 
+def test_every_status_has_its_own_message(lib):
+    codes = (cpk.QUOKA_OK, cpk.QUOKA_EINVAL, cpk.QUOKA_EUNSUPPORTED, cpk.QUOKA_EWORKSPACE,
+             cpk.QUOKA_EHIP, cpk.QUOKA_ECHECK)
+    msgs = [lib.quoka_strerror(c).decode() for c in codes]
+    assert len(set(msgs)) == len(codes) and "unknown status" not in msgs
+    assert lib.quoka_strerror(len(codes)).decode() == "unknown status"
+
+
+def test_check_selection_validates_before_any_launch(lib):
+    shape = _host_shape([0, 10], [0, 20])
+    assert lib.quoka_check_selection(ctypes.byref(shape.c), None, 8, None) == cpk.QUOKA_EINVAL
+    assert "sel_idx" in lib.quoka_last_error().decode()
+    assert lib.quoka_check_selection(ctypes.byref(shape.c), ctypes.c_void_p(16), 0,
+                                     None) == cpk.QUOKA_EINVAL
+
+
 def test_bad_offsets_are_rejected(lib):
     assert _ws_status(_host_shape([0, 10, 5], [0, 20, 30]), 8, 8)[0] == cpk.QUOKA_EINVAL
     assert _ws_status(_host_shape([1, 10], [0, 20]), 8, 8)[0] == cpk.QUOKA_EINVAL
