@@ -28,7 +28,6 @@ import chunked_prefill_kv_amd as cpk
 import oracle
 
 QCOS_TOL = 2.0 ** -22     # |c_gpu - c_oracle|: the library's stated bound on its fp32 cosines
-SCORE_TOL = {"fp32": 1e-6, "bf16": 2e-6}   # |s_gpu - s_oracle| observed (below score_bound)
 SEL_REL_BAND = 1e-5       # the stated selection tolerance, relative to the boundary value
 ATTN_TOL = {"fp32": 1e-4, "bf16": 2e-2}    # max-abs on the attention output
 
@@ -129,7 +128,10 @@ def check_selection(w, r, heads=None, seqs=None):
             s_or = oracle.key_scores(q_grp[S_gpu], kh[h0:h1, h])
             if h1 > h0:
                 err = np.max(np.abs(s_gpu - s_or))
-                assert err <= SCORE_TOL[w.dtype], f"{where}: score error {err:.3g}"
+                # the scorer's proven bound, on which the selections' exactness rests
+                # (the errors observed are 10-20 times smaller)
+                bound = score_bound(w.dtype, w.head_dim)
+                assert err <= bound, f"{where}: score error {err:.3g} (bound {bound:.3g})"
             # stage 4: kept keys
             si = r["sel_idx"][s, h]
             assert np.all(si[b_eff:] == -1), f"{where}: sel_idx padding"
@@ -290,7 +292,8 @@ def check_variant_selection(w, r, variant):
                                              f"{where} q_idx")
             s_gpu = r["scores"][h, h0:h1].astype(np.float64)
             k_h = kh[h0:h1, h]
-            tol = np.full(h1 - h0, SCORE_TOL[w.dtype])
+            tol = np.full(h1 - h0, score_bound(w.dtype, w.head_dim, G,
+                                               per_head=variant == "per_head"))
             if variant == "dot":
                 s_or = oracle.key_scores(q_grp[S_gpu], k_h, sim="dot")
                 if c1 > c0 and h1 > h0:
