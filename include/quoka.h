@@ -175,8 +175,10 @@ typedef enum quoka_variant {
   /* Scores each kept token's G query heads separately against the keys and
    * averages afterwards (G times the products; "QUOKA Explained", "A wrinkle:
    * grouped-query attention"). Same scores as QUOKA up to rounding. Needs
-   * 16 * ceil(q_budget / 16) * H_q / H_kv * head_dim * 4 + 8192 bytes of LDS
-   * per workgroup; QUOKA_EUNSUPPORTED beyond the device's limit. */
+   * 16 * ceil(q_budget / 16) * H_q / H_kv <= 640 rows and R * H_q / H_kv *
+   * head_dim * 4 + 8192 bytes of LDS per workgroup (R = 16 * ceil(q_budget /
+   * 16) in bf16, q_budget in fp32); QUOKA_EUNSUPPORTED beyond either limit
+   * (160 KB of LDS on MI355X). */
   QUOKA_VARIANT_PER_HEAD = 4,
   /* One kept-token subset per sequence, shared by all KV heads: the N_q
    * tokens with the lowest mean over KV heads of the per-head cosines ("QUOKA

@@ -7,18 +7,30 @@ histories, GQA groups from 1 to 8 including ones that do not divide a
 so that a combination nobody thought of still meets the same bar: kept sets
 exact within the stated bands, the layout invariants, every attention row of
 one (sequence, KV head) and sampled rows of the rest within the attention
-tolerance, and the fused gather bit-identical to gather + attend.
+tolerance, and the fused gather bit-identical to gather + attend. The first
+shapes also go through each baseline selection the pages compare against.
 """
 import numpy as np
 import pytest
 
+import chunked_prefill_kv_amd as cpk
 from workloads import make_case
 
-from gpu_check import check_attention, check_invariants, check_selection, run_stages, upload
+from gpu_check import (check_attention, check_invariants, check_selection,
+                       check_variant_selection, run_stages, run_variant, upload)
 
 pytestmark = pytest.mark.gpu
 
 N_CASES = 40
+N_VARIANT_CASES = 12
+
+
+def per_head_fits(nq, g, d, dt):
+    """The per-head baseline's on-chip limits (quoka.h): at most 640 padded
+    kept rows x group, and its rows plus a 2048-bin histogram in 160 KB of LDS."""
+    pad = -(-nq // 16) * 16
+    rows = pad if dt == "bf16" else nq
+    return pad * g <= 640 and rows * g * d * 4 + 8192 <= 160 * 1024
 
 
 def _draw(i):
@@ -59,3 +71,20 @@ def test_random_shape(i):
     assert np.array_equal(r["out_fused"], r["out"])
     print(f"[gpu] {name}: attention max-abs {full:.3g} (all rows of one head), "
           f"{err:.3g} (sampled)", flush=True)
+
+
+@pytest.mark.parametrize("variant", [v for v in cpk.VARIANTS if v != "quoka"])
+@pytest.mark.parametrize("i", range(N_VARIANT_CASES))
+def test_random_shape_baselines(i, variant):
+    seqs, hq, hkv, d, dt, nq, b, scaled = _draw(i)
+    name = f"sweep{i}"
+    print(f"[gpu] {name} {variant}", flush=True)
+    w = make_case(seqs, hq, hkv, d, dt, nq, b, seed=4000 + i, scaled=scaled, name=name)
+    shape, t = upload(w)
+    if variant == "per_head" and not per_head_fits(nq, hq // hkv, d, dt):
+        with pytest.raises(cpk.QuokaError) as e:
+            run_variant(w, shape, t, variant)
+        assert e.value.status == cpk.QUOKA_EUNSUPPORTED
+        return
+    r = run_variant(w, shape, t, variant)
+    check_variant_selection(w, r, variant)
