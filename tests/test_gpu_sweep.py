@@ -8,7 +8,11 @@ so that a combination nobody thought of still meets the same bar: kept sets
 exact within the stated bands, the layout invariants, every attention row of
 one (sequence, KV head) and sampled rows of the rest within the attention
 tolerance, and the fused gather bit-identical to gather + attend. The first
-shapes also go through each baseline selection the pages compare against.
+shapes also go through each baseline selection the pages compare against. A
+few large shapes (chunks up to 4096 tokens, histories up to 64K keys, bf16)
+reach the launch modes only large batches take: eight-wave attention
+workgroups in the paired and the contiguous orders, and scorer tiles of up to
+2048 keys.
 """
 import numpy as np
 import pytest
@@ -23,6 +27,7 @@ pytestmark = pytest.mark.gpu
 
 N_CASES = 40
 N_VARIANT_CASES = 12
+N_LARGE_CASES = 6
 
 
 def per_head_fits(nq, g, d, dt):
@@ -88,3 +93,31 @@ def test_random_shape_baselines(i, variant):
         return
     r = run_variant(w, shape, t, variant)
     check_variant_selection(w, r, variant)
+
+
+def _draw_large(i):
+    rng = np.random.default_rng(9500 + i)
+    S = int(rng.integers(1, 5))
+    seqs = [(int(rng.integers(1, 4097)), int(rng.integers(0, 65537))) for _ in range(S)]
+    hkv = int(rng.choice([2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 7, 8]))
+    d = int(rng.choice([64, 128]))
+    nq = int(rng.integers(1, 129))
+    b = int(rng.integers(1, 4097))
+    return seqs, hkv * g, hkv, d, "bf16", nq, b, bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("i", range(N_LARGE_CASES))
+def test_random_large_shape(i):
+    seqs, hq, hkv, d, dt, nq, b, scaled = _draw_large(i)
+    name = f"large{i}"
+    print(f"[gpu] {name}: seqs={seqs} Hq={hq} Hkv={hkv} d={d} {dt} Nq={nq} B={b} "
+          f"scaled={scaled}", flush=True)
+    w = make_case(seqs, hq, hkv, d, dt, nq, b, seed=5000 + i, scaled=scaled, name=name)
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    check_invariants(w, r)
+    check_selection(w, r)
+    err = check_attention(w, r, rows=48, rng=np.random.default_rng(i))
+    assert np.array_equal(r["out_fused"], r["out"])
+    print(f"[gpu] {name}: attention max-abs {err:.3g} (sampled)", flush=True)
