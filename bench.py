@@ -17,7 +17,7 @@ the first pass) and gives the stage times and the roofline entry for the
 dominant kernel (chunk attention, bf16 MFMA). cpu_baseline times the fp64
 oracle on a bounded sample of the same workload on the host cores.
 
-usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config long]
+usage: python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--config long]
 """
 from __future__ import annotations
 
