@@ -12,7 +12,8 @@ shapes also go through each baseline selection the pages compare against. A
 few large shapes (chunks up to 4096 tokens, histories up to 64K keys, bf16)
 reach the launch modes only large batches take: eight-wave attention
 workgroups in the paired and the contiguous orders, and scorer tiles of up to
-2048 keys.
+2048 keys. Two limit shapes: a chunk longer than the cosines the query select
+holds on chip, and a 600K-key history.
 """
 import numpy as np
 import pytest
@@ -119,5 +120,28 @@ def test_random_large_shape(i):
     check_invariants(w, r)
     check_selection(w, r)
     err = check_attention(w, r, rows=48, rng=np.random.default_rng(i))
+    assert np.array_equal(r["out_fused"], r["out"])
+    print(f"[gpu] {name}: attention max-abs {err:.3g} (sampled)", flush=True)
+
+
+LIMIT_CASES = {
+    # a chunk longer than the 12288 cosines the query select stages on chip
+    # (it then reads them from the workspace), with the maximum query budget
+    "chunk_past_lds": ([(13000, 3000)], 4, 1, 64, "bf16", 128, 512),
+    # a 600K-key history: hundreds of scorer and top-B tiles per head
+    "history_600k": ([(64, 600000)], 8, 2, 128, "bf16", 16, 4096),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LIMIT_CASES))
+def test_limit_shape(name):
+    seqs, hq, hkv, d, dt, nq, b = LIMIT_CASES[name]
+    print(f"[gpu] {name}: seqs={seqs} Hq={hq} Hkv={hkv} d={d} {dt} Nq={nq} B={b}", flush=True)
+    w = make_case(seqs, hq, hkv, d, dt, nq, b, seed=6000, name=name)
+    shape, t = upload(w)
+    r = run_stages(w, shape, t)
+    check_invariants(w, r)
+    check_selection(w, r)
+    err = check_attention(w, r, rows=64, rng=np.random.default_rng(1))
     assert np.array_equal(r["out_fused"], r["out"])
     print(f"[gpu] {name}: attention max-abs {err:.3g} (sampled)", flush=True)
