@@ -85,6 +85,21 @@ def gather_bytes(w) -> float:
     return _elem(w) * w.head_dim * 2 * (sel + rows) + 4 * rows
 
 
+def attention_kernel_name(w) -> str:
+    """The attention kernel the library launches for this layer: the fp32 VALU kernel, the
+    16-rows-per-wave kernel where 32-row four-wave tiles would be between 129 and 256 (at
+    most one per CU, no key split), else the 32-row kernel (the library's attention plan;
+    this only names the kernel in the roofline entry)."""
+    if w.dtype != "bf16":
+        return "attn_valu_kernel"
+    G = w.num_q_heads // w.num_kv_heads
+    maxc = int(np.max(np.diff(w.cu_chunk)))
+    rows = maxc * G
+    grid4 = (rows + 127) // 128 * w.num_kv_heads * w.num_seqs
+    many = (rows + 255) // 256 * w.num_kv_heads * w.num_seqs >= 512
+    return "attn_r16_kernel" if (not many and 128 < grid4 <= 256) else "attn_mfma_kernel"
+
+
 def measured_traffic(config: str, kernel: str, source: str):
     """HBM bytes per launch from the committed counter runs (profiles/hbm_traffic.md), or
     None when they are missing or the kernel source changed since they were taken."""
@@ -424,7 +439,7 @@ def main():
     flops = attention_flops(w)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     achieved = flops / (att_us * 1e-6) / 1e12
-    attn_kernel = "attn_mfma_kernel" if w.dtype == "bf16" else "attn_valu_kernel"
+    attn_kernel = attention_kernel_name(w)
     traffic = measured_traffic(args.config, attn_kernel, "attention.hip")
     gbytes = gather_bytes(w)
     line = {

@@ -495,6 +495,274 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA path with 16 rows per wave (v_mfma_f32_16x16x32_bf16), eight waves per
+// 128-row tile: for shapes with at most one four-wave tile per CU, where the
+// 32-row kernel leaves a single wave per SIMD to run its chain of dependent
+// 64-key steps alone; here every SIMD holds two waves of half the work.
+//   S^T = K Q^T : A = 16 keys x 32 d of the K tile (LDS), B = the wave's Q
+//                 (registers); C lane l = query row l%16, keys (l/16)*4..+3
+//                 of each 16-key block.
+//   O^T += V^T P^T per 32-key step: B = P straight from the S^T accumulators
+//                 of its two 16-key blocks (lane l holds keys (l/16)*4..+3 of
+//                 each, which is the MFMA's k-slice (l/16)*8..+7 under a
+//                 fixed permutation of the step's keys); A = V^T read
+//                 transposed for the same permutation (two 4-key reads).
+// Tile order, masks, lazy rescaling, loads and the fused gather are as in
+// attn_mfma_kernel; V rows are swizzled so that each 32-lane group of a
+// transposing read (8 keys x 2 chunks) covers all 64 banks once. Every wave
+// reads the whole K and V tile for half the rows of the 32-row kernel, so the
+// LDS carries twice the bytes per product: worth it only where the 32-row
+// kernel has a single wave per SIMD (narrow layer: 53.6 -> 49.2 us; four-wave
+// 64-row tiles, two per CU, measured the same 49.4 us).
+// ---------------------------------------------------------------------------
+template <int D, int NW, bool kIdx>
+__global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_r16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k_sel, const bf16* __restrict__ v_sel,
+    const int32_t* __restrict__ sel, const bf16* __restrict__ k_chunk, const bf16* __restrict__ v_chunk,
+    const int32_t* __restrict__ cu_chunk, const int32_t* __restrict__ cu_hist, int S, int Hq,
+    int Hkv, int G, int kv_budget, int ntile_max, float scale_log2, bf16* __restrict__ out) {
+  constexpr int KT = kAttnKeys, NDS = D / 32, NDB = D / 16, TR = NW * 16;  // TR rows per tile
+  __shared__ __attribute__((aligned(1024))) bf16 Ks0[KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks1[KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs0[KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs1[KT * D];
+
+  const int nblk = ntile_max * Hkv * S;
+  const int Lb = blockIdx.x;
+  const int qx = nblk / kXcds, rx = nblk % kXcds, x = Lb % kXcds, slot = Lb / kXcds;
+  const int logical = x < rx ? x * (qx + 1) + slot : rx * (qx + 1) + (x - rx) * qx + slot;
+  const int bx = logical % ntile_max;
+  const int h = (logical / ntile_max) % Hkv;
+  const int s = logical / (ntile_max * Hkv);
+
+  const int c_off = cu_chunk[s];
+  const int C = cu_chunk[s + 1] - c_off;
+  const int rows = C * G;
+  const int ntr = (rows + TR - 1) / TR;
+  if (bx >= ntr) return;
+  const int tile = ntr - 1 - bx;  // longest rows (most keys) first
+  const int h_off = cu_hist[s];
+  const int Lh = cu_hist[s + 1] - h_off;
+  const int B_eff = min(kv_budget, Lh);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rl = lane & 15, g4 = lane >> 4;
+  const int row0 = tile * TR + wave * 16;  // the wave's first row
+  const bool wave_live = row0 < rows;
+  const int r = row0 + rl;
+  const bool rvalid = r < rows;
+  const int t = rvalid ? r / G : 0;
+  const int jh = h * G + (rvalid ? r % G : 0);
+  const int t_wave_first = min(C - 1, row0 / G);
+  const int t_wave_last = min(C - 1, (row0 + 15) / G);
+
+  // B operand of S^T: lane l holds Q[row l%16][ds*32 + (l/16)*8 ..+7]
+  bf16x8 qreg[NDS];
+  {
+    const bf16* qrow = q + ((int64_t)(c_off + t) * Hq + jh) * D + g4 * 8;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const bf16x8 v = *(const bf16x8*)(qrow + ds * 32);
+      qreg[ds] = rvalid ? v : (bf16x8){};
+    }
+  }
+  const int t_last = min(C - 1, (tile * TR + TR - 1) / G);  // the workgroup's last token
+  f32x4 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  const int64_t prob = (int64_t)s * Hkv + h;
+  const bf16* k1 = kIdx ? k_sel + ((int64_t)h_off * Hkv + h) * D : k_sel + prob * kv_budget * D;
+  const bf16* v1 = kIdx ? v_sel + ((int64_t)h_off * Hkv + h) * D : v_sel + prob * kv_budget * D;
+  const bf16* k2 = k_chunk + ((int64_t)c_off * Hkv + h) * D;
+  const bf16* v2 = v_chunk + ((int64_t)c_off * Hkv + h) * D;
+  const int n1 = (B_eff + KT - 1) / KT;
+  const int n_all = n1 + (t_last + KT) / KT;
+  const uint32_t rb1 = kIdx ? (uint32_t)Hkv * D * 2u : D * 2u;
+  const uint32_t rb2 = (uint32_t)Hkv * D * 2u;
+  const uint32_t end1 = kIdx ? (Lh > 0 ? (uint32_t)(Lh - 1) * rb1 + D * 2u : 0u)
+                             : (uint32_t)B_eff * rb1;
+  const uint32_t end2 = (uint32_t)t_last * rb2 + D * 2u;
+  const int32_t* sidx = sel + prob * kv_budget;
+
+  // LDS slot of 16-byte chunk c of row rr: c ^ kswz(rr) for K, c ^ vswz(rr)
+  // for V. A K read (16 lanes: 16 rows, one chunk) and a V transposing read
+  // (32 lanes: 8 rows, two adjacent chunks) then cover all 64 banks once.
+  constexpr int CPR = D / 8, RPP = 64 / CPR, NP = KT / RPP / NW;
+  auto kswz = [](int rr) { return D == 128 ? (rr & 15) : ((rr >> 1) & 7); };
+  auto vswz = [](int rr) { return D == 128 ? 2 * (rr & 7) : 2 * ((rr >> 1) & 3); };
+  static_assert(NP >= 1 && KT % (RPP * NW) == 0, "tile must split into whole pieces per wave");
+  int prow[NP];
+  uint32_t kcol[NP], vcol[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int rr = (wave * NP + u) * RPP + lane / CPR, sl = lane % CPR;
+    prow[u] = rr;
+    kcol[u] = (uint32_t)(sl ^ kswz(rr)) * 16u;
+    vcol[u] = (uint32_t)(sl ^ vswz(rr)) * 16u;
+  }
+  int nidx[NP];
+  auto fetch_idx = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int key = it * KT + prow[u];
+      nidx[u] = key < B_eff ? sidx[key] : -1;
+    }
+  };
+  if (kIdx && 0 < n1) fetch_idx(0);
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  auto load = [&](int it, bf16* kd, bf16* vd) __attribute__((always_inline)) {
+    const bool ph1 = it < n1;
+    const int kbase = (ph1 ? it : it - n1) * KT;
+    if (kIdx && ph1) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k1, end1), rv = make_rsrc(v1, end1);
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int row = nidx[u];
+        const bool ok = (unsigned)row < (unsigned)Lh;
+        const uint32_t base = (uint32_t)row * rb1;
+        bf16* kp = kd + (wave * NP + u) * 512;
+        bf16* vp = vd + (wave * NP + u) * 512;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(ok ? base + kcol[u] : end1), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(ok ? base + vcol[u] : end1), 0, 0, 0);
+      }
+      if (it + 1 < n1) fetch_idx(it + 1);
+      return;
+    }
+    const uint32_t rb = ph1 ? rb1 : rb2;
+    const uint32_t skip = (uint32_t)kbase * rb;
+    const uint32_t left = (ph1 ? end1 : end2) - skip;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2), left);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2), left);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const uint32_t base = (uint32_t)prow[u] * rb;
+      bf16* kp = kd + (wave * NP + u) * 512;
+      bf16* vp = vd + (wave * NP + u) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(base + kcol[u]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(base + vcol[u]), 0, 0, 0);
+    }
+  };
+  if (0 < n_all) load(0, Ks0, Vs0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // K operand of (key block kb, d-step ds): row kb*16 + l%16, chunk
+  // ds*4 + l/16 (kb*16 leaves kswz unchanged)
+  int koff[NDS];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) koff[ds] = rl * D + (((ds * 4 + g4) ^ kswz(rl)) << 3);
+  // V^T operand of d-block db: 16-lane group g reads keys g*4 + j/4 (+16 for
+  // the second half of the step), columns db*16 + 4 (j%4), j = l%16
+  int voff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int row = g4 * 4 + (rl >> 2);
+    const int c = db * 2 + ((rl & 3) >> 1);
+    voff[db] = row * D + ((c ^ vswz(row)) << 3) + 4 * (rl & 1);
+  }
+  const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+
+  auto step = [&](int it, auto Bc) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
+    const bf16* ks = B ? Ks1 : Ks0;
+    const bf16* vs = B ? Vs1 : Vs0;
+    if (it + 1 < n_all) load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
+    const bool ph1 = it < n1;
+    const int kbase = (ph1 ? it : it - n1) * KT;
+    if (wave_live && (ph1 || kbase <= t_wave_last)) {
+      f32x4 sacc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sacc[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        bf16x8 ka[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) ka[kb] = *(const bf16x8*)(ks + kb * 16 * D + koff[ds]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qreg[ds], sacc[kb], 0, 0, 0);
+      }
+      const bool need_mask = ph1 ? (kbase + KT > B_eff) : (kbase + KT - 1 > t_wave_first);
+      if (need_mask) {
+        const int lim = (ph1 ? B_eff - 1 : t) - kbase - g4 * 4;  // visible: offset <= lim
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kb * 16 + e > lim) sacc[kb][e] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
+      mx = rows_max(mx);  // the four lanes of the row
+      const float m_cand = fmaxf(m_run, mx);
+      const bool upd = (m_cand - m_run) * scale_log2 > 32.0f;
+      if (__ballot(upd)) {
+        const float m_new = upd ? m_cand : m_run;
+        const float alpha = upd ? __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2) : 1.f;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float base = m_run == -INFINITY ? 0.f : m_run * scale_log2;
+      // P of the 32-key step ks: keys g*4..+3 of block 2ks, then of block 2ks + 1
+      bf16x8 pb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[ks][e] = (bf16)__builtin_amdgcn_exp2f(
+              fmaf(sacc[2 * ks + (e >> 2)][e & 3], scale_log2, -base));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 v = pb[ks];
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, l_part, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, l_part, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, l_part, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, l_part, false);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 a[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16* p0 = vs + ks * 32 * D + voff[db];
+          const bf16x4 lo4 = lds_read_tr16(p0);
+          const bf16x4 hi4 = lds_read_tr16(p0 + 16 * D);
+          a[db] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[db], pb[ks], oacc[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  for (int it = 0; it < n_all; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_all) step(it + 1, std::integral_constant<int, 1>{});
+  }
+
+  const float l_run = rows_sum(l_part);
+  if (rvalid) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    bf16* orow = out + ((int64_t)(c_off + t) * Hq + jh) * D + g4 * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][e] * inv);
+      *(bf16x4*)(orow + db * 16) = v;
+    }
+  }
+}
+
 // Combination of the key ranges' states of a row (the online softmax's merge
 // step): with b = the largest reference max (log2 units),
 // O = sum_r 2^(b_r - b) O_r / sum_r 2^(b_r - b) l_r. A range that saw no key
@@ -545,6 +813,7 @@ namespace {
 
 struct AttnPlan {
   int nw, pair, ntile, nsplit;
+  bool r16;  // 16 rows per wave (attn_r16_kernel)
 };
 
 AttnPlan attn_plan(const Problem& p) {
@@ -577,7 +846,10 @@ AttnPlan attn_plan(const Problem& p) {
     const int64_t steps = (p.kv_budget + 63) / 64 + (p.maxC + 63) / 64;
     nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({256 / grid4, steps, kAttnMaxSplit}));
   }
-  return {nw, pair, ntile, nsplit};
+  // at most one four-wave tile per CU and no key split: sixteen rows per wave,
+  // eight waves per tile, so that every SIMD runs two waves
+  const bool r16 = nw == 4 && nsplit == 1 && grid4 <= 256;
+  return {nw, pair, ntile, nsplit, r16};
 }
 
 }  // namespace
@@ -613,10 +885,16 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
                      (const bf16*)k_sel, (const bf16*)v_sel, sel, (const bf16*)k_chunk,           \
                      (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,          \
                      p.kv_budget, ntile * nsplit, pair, sl2, nsplit, part_o, part_ml, (bf16*)out)
-#define QUOKA_ATTN_NW(D, IDX) { if (nw == 8) QUOKA_ATTN(D, 8, IDX); else QUOKA_ATTN(D, 4, IDX); }
+#define QUOKA_ATTN_R16(D, IDX)                                                                 \
+  hipLaunchKernelGGL((attn_r16_kernel<D, 8, IDX>), grid, dim3(512), 0, st, (const bf16*)q,      \
+                     (const bf16*)k_sel, (const bf16*)v_sel, sel, (const bf16*)k_chunk,           \
+                     (const bf16*)v_chunk, p.cu_chunk, p.cu_hist, p.S, p.Hq, p.Hkv, p.G,          \
+                     p.kv_budget, ntile, sl2, (bf16*)out)
+#define QUOKA_ATTN_NW(D, IDX) { if (a.r16) QUOKA_ATTN_R16(D, IDX); else if (nw == 8) QUOKA_ATTN(D, 8, IDX); else QUOKA_ATTN(D, 4, IDX); }
     if (sel) { if (p.D == 128) QUOKA_ATTN_NW(128, true) else QUOKA_ATTN_NW(64, true) }
     else     { if (p.D == 128) QUOKA_ATTN_NW(128, false) else QUOKA_ATTN_NW(64, false) }
 #undef QUOKA_ATTN_NW
+#undef QUOKA_ATTN_R16
 #undef QUOKA_ATTN
     if (nsplit > 1) {
       const int64_t nthr = nrow * (p.D / 8);

@@ -38,7 +38,8 @@ CASES = {
     "bf16_decode_g4": ([(1, 3000), (1, 0), (2, 500), (1, 64)], 8, 2, 128, "bf16", 1, 256, {}),
     "bf16_decode_g8": ([(1, 1500), (1, 70)], 16, 2, 128, "bf16", 2, 1000, dict(scaled=True)),
     "bf16_decode_d64_g1": ([(1, 2000), (1, 100), (1, 1)], 2, 2, 64, "bf16", 1, 300, {}),
-    # 140 four-wave attention tiles: the unsplit four-wave order (at most 128
+    # 140 128-row attention tiles (between 128 and 256: at most one per CU, no
+    # key split): sixteen rows per wave, eight waves per tile (at most 128
     # tiles split their keys into ranges and merge, as every smaller case here)
     "bf16_four_wave_unsplit": ([(1100, 1500)], 16, 4, 128, "bf16", 16, 200, {}),
     # scorer tiles of 1024 keys (four streamed blocks per wave), last tile partial
@@ -191,6 +192,13 @@ ORDER_CASES = {
     # the tokens of a tile's first rows (those rows see no key in them), and the
     # short tiles leave some ranges empty
     "split6_chunk": ([(300, 100)], 8, 2, 128, "bf16", 8, 64),
+    # sixteen rows per wave (156 tiles of 128 rows, one per CU at most): GQA 7,
+    # a partly filled last tile; and head_dim 64 over two sequences (152 tiles)
+    "r16_g7": ([(700, 900)], 28, 4, 128, "bf16", 16, 256),
+    "r16_d64": ([(600, 700), (300, 400)], 16, 4, 64, "bf16", 8, 128),
+    # 560 four-wave tiles, too few for eight-wave workgroups and more than two
+    # per CU: the unsplit four-wave kernel with 32 rows per wave
+    "four_wave_32rows": ([(1100, 800)] * 4, 16, 4, 128, "bf16", 8, 256),
     # GQA 7: 128-row tiles cut through a token's heads (paired order, 66 tiles)
     "pair_g7": ([(1200, 3000)], 28, 4, 128, "bf16", 16, 512),
     # enough tiles for eight-wave workgroups, but a chunk of at most half the
