@@ -140,6 +140,128 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Logical id of this block: linear block L runs on XCD L % 8, and XCD x is
+// given a contiguous range of logical ids (so a KV head's tiles share an L2).
+__device__ __forceinline__ int xcd_logical_block(int nblk) {
+  const int L = blockIdx.x;
+  const int qx = nblk / kXcds, rx = nblk % kXcds, x = L % kXcds, slot = L / kXcds;
+  return x < rx ? x * (qx + 1) + slot : rx * (qx + 1) + (x - rx) * qx + slot;
+}
+
+// LDS slot of the 16-byte chunk c of K/V tile row r: c ^ k(r) for K, c ^ v(r)
+// for V. LDS serves 64 4-byte banks; a 16-byte read takes 16 lanes at a time
+// and an 8-byte transposing read 32, and a group whose lanes share a bank
+// pays an extra cycle (both measured on the chip: with c ^ (r & 7) every K
+// read of 16 rows paid 4 extra cycles, with c ^ 2(r & 3) every V read of
+// 4 rows x 4 chunks 2). K: a read of 16 rows (one chunk each) covers all 64
+// banks. V, kR16 = false: a 32-lane transposing read of 4 rows x 4 chunks
+// (32 rows per wave); kR16 = true: of 8 rows x 2 chunks (16 rows per wave).
+template <int D, bool kR16>
+struct KVSwizzle {
+  __device__ static int k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int v(int r) {
+    if constexpr (kR16) return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+    else return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
+  }
+};
+
+// The K/V tiles of one (sequence, KV head) for a workgroup of NW waves, 64
+// keys per tile: first the kept history (k_sel / v_sel rows, or with kIdx the
+// rows of k_hist / v_hist that the kept indices name: the gather fused in),
+// then the chunk's own keys up to the workgroup's last token t_last. Tiles
+// arrive by buffer loads that write LDS directly (a wave instruction fills
+// 1 KB, lane l at +16 l, i.e. RPP rows of CPR 16-byte chunks; lane l of piece
+// P takes row P*RPP + l/CPR and fetches the chunk that belongs in slot l%CPR),
+// so no registers stage them; reads past the valid rows (the tail past B_eff,
+// index -1) fall outside the buffer resource and write zeros. With kIdx the
+// history row indices are fetched one tile ahead, so that a row load never
+// waits for its own index load.
+template <int D, int NW, bool kIdx, bool kR16>
+struct KVTiles {
+  static constexpr int KT = kAttnKeys, CPR = D / 8, RPP = 64 / CPR, NP = KT / RPP / NW;
+  static_assert(NP >= 1 && KT % (RPP * NW) == 0, "tile must split into whole pieces per wave");
+  using Swz = KVSwizzle<D, kR16>;
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  const bf16 *k1, *v1, *k2, *v2;
+  const int32_t* sidx;
+  uint32_t rb1, rb2, end1, end2;
+  int n1, B_eff, Lh, wave;
+  int prow[NP], nidx[NP];
+  uint32_t kcol[NP], vcol[NP];
+
+  __device__ __forceinline__ KVTiles(const bf16* k_sel, const bf16* v_sel, const int32_t* sel,
+                                     const bf16* k_chunk, const bf16* v_chunk, int s, int h,
+                                     int Hkv, int c_off, int h_off, int Lh_, int kv_budget,
+                                     int t_last, int wave_) {
+    const int64_t prob = (int64_t)s * Hkv + h;
+    Lh = Lh_;
+    B_eff = min(kv_budget, Lh);
+    wave = wave_;
+    k1 = kIdx ? k_sel + ((int64_t)h_off * Hkv + h) * D : k_sel + prob * kv_budget * D;
+    v1 = kIdx ? v_sel + ((int64_t)h_off * Hkv + h) * D : v_sel + prob * kv_budget * D;
+    k2 = k_chunk + ((int64_t)c_off * Hkv + h) * D;
+    v2 = v_chunk + ((int64_t)c_off * Hkv + h) * D;
+    n1 = (B_eff + KT - 1) / KT;
+    rb1 = kIdx ? (uint32_t)Hkv * D * 2u : D * 2u;  // row bytes
+    rb2 = (uint32_t)Hkv * D * 2u;
+    end1 = kIdx ? (Lh > 0 ? (uint32_t)(Lh - 1) * rb1 + D * 2u : 0u)  // valid bytes
+                : (uint32_t)B_eff * rb1;
+    end2 = (uint32_t)t_last * rb2 + D * 2u;
+    sidx = sel + prob * kv_budget;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int r = (wave * NP + u) * RPP + lane / CPR, sl = lane % CPR;
+      prow[u] = r;
+      kcol[u] = (uint32_t)(sl ^ Swz::k(r)) * 16u;
+      vcol[u] = (uint32_t)(sl ^ Swz::v(r)) * 16u;
+    }
+  }
+  // history row indices of tile it
+  __device__ __forceinline__ void fetch_idx(int it) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int key = it * KT + prow[u];
+      nidx[u] = key < B_eff ? sidx[key] : -1;
+    }
+  }
+  // tile it into kd / vd (with kIdx, tile it's indices fetched beforehand)
+  __device__ __forceinline__ void load(int it, bf16* kd, bf16* vd) {
+    const bool ph1 = it < n1;
+    const int kbase = (ph1 ? it : it - n1) * KT;
+    if (kIdx && ph1) {
+      // row of key kbase + r is history row sel[kbase + r]; padding (-1) and
+      // out-of-range indices read at the end of the buffer, i.e. as zeros
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k1, end1), rv = make_rsrc(v1, end1);
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int row = nidx[u];
+        const bool ok = (unsigned)row < (unsigned)Lh;
+        const uint32_t base = (uint32_t)row * rb1;
+        bf16* kp = kd + (wave * NP + u) * 512;
+        bf16* vp = vd + (wave * NP + u) * 512;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(ok ? base + kcol[u] : end1), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(ok ? base + vcol[u] : end1), 0, 0, 0);
+      }
+      if (it + 1 < n1) fetch_idx(it + 1);
+      return;
+    }
+    const uint32_t rb = ph1 ? rb1 : rb2;
+    const uint32_t skip = (uint32_t)kbase * rb;
+    const uint32_t left = (ph1 ? end1 : end2) - skip;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2), left);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2), left);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const uint32_t base = (uint32_t)prow[u] * rb;
+      bf16* kp = kd + (wave * NP + u) * 512;
+      bf16* vp = vd + (wave * NP + u) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(base + kcol[u]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(base + vcol[u]), 0, 0, 0);
+    }
+  }
+};
+
 template <int D, int NW, bool kIdx>
 __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k_sel, const bf16* __restrict__ v_sel,
@@ -155,13 +277,9 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Vs0[KT * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vs1[KT * D];
 
-  // XCD-aware renumbering: linear block L runs on XCD L % 8; give XCD x a
-  // contiguous range of logical ids (key range fastest, then tile, then head,
-  // then sequence). ntile_max counts (tile, key range) units.
-  const int nblk = ntile_max * Hkv * S;
-  const int L = blockIdx.x;
-  const int qx = nblk / kXcds, rx = nblk % kXcds, x = L % kXcds, slot = L / kXcds;
-  const int logical = x < rx ? x * (qx + 1) + slot : rx * (qx + 1) + (x - rx) * qx + slot;
+  // logical ids: key range fastest, then tile, then head, then sequence;
+  // ntile_max counts (tile, key range) units
+  const int logical = xcd_logical_block(ntile_max * Hkv * S);
   const int bxs = logical % ntile_max;
   const int bx = bxs / nsplit, sigma = bxs % nsplit;
   const int h = (logical / ntile_max) % Hkv;
@@ -225,115 +343,36 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
   for (int db = 0; db < NDB; ++db) oacc[db] = (f32x16){};
   float m_run = -INFINITY, l_part = 0.f;
 
-  const int64_t prob = (int64_t)s * Hkv + h;
-  // history rows: the kept rows of k_sel / v_sel, or (kIdx) rows sel[b] of
-  // this sequence's k_hist / v_hist, passed in their place (gather fused in)
-  const bf16* k1 = kIdx ? k_sel + ((int64_t)h_off * Hkv + h) * D : k_sel + prob * kv_budget * D;
-  const bf16* v1 = kIdx ? v_sel + ((int64_t)h_off * Hkv + h) * D : v_sel + prob * kv_budget * D;
-  const bf16* k2 = k_chunk + ((int64_t)c_off * Hkv + h) * D;
-  const bf16* v2 = v_chunk + ((int64_t)c_off * Hkv + h) * D;
-  const int n1 = (B_eff + KT - 1) / KT;
+  KVTiles<D, NW, kIdx, false> kv(k_sel, v_sel, sel, k_chunk, v_chunk, s, h, Hkv, c_off, h_off,
+                                  Lh, kv_budget, t_last, wave);
+  const int n1 = kv.n1;
   const int n_all = n1 + (t_last + KT) / KT;
   // with nsplit > 1 this workgroup takes the sigma-th of nsplit near-equal
   // ranges of the n_all key tiles
   const int it0 = (int)((int64_t)sigma * n_all / nsplit);
   const int it1 = (int)((int64_t)(sigma + 1) * n_all / nsplit);
-  const uint32_t rb1 = kIdx ? (uint32_t)Hkv * D * 2u : D * 2u;           // row bytes
-  const uint32_t rb2 = (uint32_t)Hkv * D * 2u;
-  const uint32_t end1 = kIdx ? (Lh > 0 ? (uint32_t)(Lh - 1) * rb1 + D * 2u : 0u)  // valid bytes
-                             : (uint32_t)B_eff * rb1;
-  const uint32_t end2 = (uint32_t)t_last * rb2 + D * 2u;
-  const int32_t* sidx = sel + prob * kv_budget;
-
-  // Direct loads: a wave instruction writes 1 KB of LDS (lane l at +16 l),
-  // i.e. RPP rows of CPR 16-byte chunks; lane l of piece P takes row
-  // P*RPP + l/CPR and fetches the chunk that belongs in slot l%CPR: chunk
-  // slot ^ kswz(row) for K, slot ^ vswz(row) for V. LDS serves 64 4-byte
-  // banks; a 16-byte read takes 16 lanes at a time and an 8-byte transposing
-  // read 32, and a group whose lanes share a bank pays an extra cycle (both
-  // measured on the chip: with slot ^ (row & 7) every K read of 16 rows paid
-  // 4 extra cycles, with slot ^ 2(row & 3) every V read of 4 rows x 4 chunks
-  // 2). The swizzles spread the 16 rows of a K read over all 64 banks and
-  // the 4 x 4 chunks of a V read likewise.
-  constexpr int CPR = D / 8, RPP = 64 / CPR, NP = KT / RPP / NW;  // pieces per wave per tensor
-  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
-  auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 2 * (r & 3); };
-  static_assert(NP >= 1 && KT % (RPP * NW) == 0, "tile must split into whole pieces per wave");
-  int prow[NP];
-  uint32_t kcol[NP], vcol[NP];
-#pragma unroll
-  for (int u = 0; u < NP; ++u) {
-    const int r = (wave * NP + u) * RPP + lane / CPR, sl = lane % CPR;
-    prow[u] = r;
-    kcol[u] = (uint32_t)(sl ^ kswz(r)) * 16u;
-    vcol[u] = (uint32_t)(sl ^ vswz(r)) * 16u;
-  }
-  // kIdx: history row indices of the next tile to load, fetched one tile
-  // ahead so that a row load never waits for its own index load
-  int nidx[NP];
-  auto fetch_idx = [&](int it) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int key = it * KT + prow[u];
-      nidx[u] = key < B_eff ? sidx[key] : -1;
-    }
-  };
-  if (kIdx && it0 < n1) fetch_idx(it0);
-  using lds_ptr = __attribute__((address_space(3))) void*;
-  auto load = [&](int it, bf16* kd, bf16* vd) __attribute__((always_inline)) {
-    const bool ph1 = it < n1;
-    const int kbase = (ph1 ? it : it - n1) * KT;
-    if (kIdx && ph1) {
-      // row of key kbase + r is history row sel[kbase + r]; padding (-1) and
-      // out-of-range indices read at the end of the buffer, i.e. as zeros
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k1, end1), rv = make_rsrc(v1, end1);
-#pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        const int row = nidx[u];
-        const bool ok = (unsigned)row < (unsigned)Lh;
-        const uint32_t base = (uint32_t)row * rb1;
-        bf16* kp = kd + (wave * NP + u) * 512;
-        bf16* vp = vd + (wave * NP + u) * 512;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(ok ? base + kcol[u] : end1), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(ok ? base + vcol[u] : end1), 0, 0, 0);
-      }
-      if (it + 1 < n1) fetch_idx(it + 1);
-      return;
-    }
-    const uint32_t rb = ph1 ? rb1 : rb2;
-    const uint32_t skip = (uint32_t)kbase * rb;
-    const uint32_t left = (ph1 ? end1 : end2) - skip;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2), left);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2), left);
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const uint32_t base = (uint32_t)prow[u] * rb;
-      bf16* kp = kd + (wave * NP + u) * 512;
-      bf16* vp = vd + (wave * NP + u) * 512;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(base + kcol[u]), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(base + vcol[u]), 0, 0, 0);
-    }
-  };
-  if (it0 < it1) load(it0, Ks0, Vs0);
+  using Swz = KVSwizzle<D, false>;
+  if (kIdx && it0 < n1) kv.fetch_idx(it0);
+  if (it0 < it1) kv.load(it0, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // lane-constant parts of the LDS read addresses
   const int g16 = lane >> 4, j16 = lane & 15;
   // K operand of d-step ds: row sb*32 + col, chunk 2 ds + hi stored at
-  // slot (2 ds + hi) ^ kswz(col) (sb*32 leaves kswz unchanged)
+  // slot (2 ds + hi) ^ k(col) (sb*32 leaves the swizzle unchanged)
   int koff[NDS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) koff[ds] = col * D + (((2 * ds + hi) ^ kswz(col)) << 3);
+  for (int ds = 0; ds < NDS; ++ds) koff[ds] = col * D + (((2 * ds + hi) ^ Swz::k(col)) << 3);
   // V transpose reads: row hi*4 + j16/4 (+ tile offsets, all multiples of 8,
-  // which leave vswz unchanged), columns db*32 + (g16&1)*16 + 4(j16&3);
-  // chunk c sits at c ^ vswz(row)
+  // which leave the swizzle unchanged), columns db*32 + (g16&1)*16 + 4(j16&3);
+  // chunk c sits at c ^ v(row)
   int voff[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int c = db * 4 + (g16 & 1) * 2 + ((j16 & 3) >> 1);
     const int row = hi * 4 + (j16 >> 2);
-    voff[db] = row * D + ((c ^ vswz(row)) << 3) + 4 * (j16 & 1);
+    voff[db] = row * D + ((c ^ Swz::v(row)) << 3) + 4 * (j16 & 1);
   }
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
@@ -342,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_mfma_kernel(
     constexpr int B = decltype(Bc)::value;
     bf16* kcur = B ? Ks1 : Ks0;
     bf16* vcur = B ? Vs1 : Vs0;
-    if (it + 1 < it1) load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
+    if (it + 1 < it1) kv.load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
     const bf16* ks = kcur;
@@ -528,10 +567,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_r16_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Vs0[KT * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vs1[KT * D];
 
-  const int nblk = ntile_max * Hkv * S;
-  const int Lb = blockIdx.x;
-  const int qx = nblk / kXcds, rx = nblk % kXcds, x = Lb % kXcds, slot = Lb / kXcds;
-  const int logical = x < rx ? x * (qx + 1) + slot : rx * (qx + 1) + (x - rx) * qx + slot;
+  const int logical = xcd_logical_block(ntile_max * Hkv * S);
   const int bx = logical % ntile_max;
   const int h = (logical / ntile_max) % Hkv;
   const int s = logical / (ntile_max * Hkv);
@@ -573,87 +609,21 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_r16_kernel(
   for (int db = 0; db < NDB; ++db) oacc[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
 
-  const int64_t prob = (int64_t)s * Hkv + h;
-  const bf16* k1 = kIdx ? k_sel + ((int64_t)h_off * Hkv + h) * D : k_sel + prob * kv_budget * D;
-  const bf16* v1 = kIdx ? v_sel + ((int64_t)h_off * Hkv + h) * D : v_sel + prob * kv_budget * D;
-  const bf16* k2 = k_chunk + ((int64_t)c_off * Hkv + h) * D;
-  const bf16* v2 = v_chunk + ((int64_t)c_off * Hkv + h) * D;
-  const int n1 = (B_eff + KT - 1) / KT;
+  KVTiles<D, NW, kIdx, true> kv(k_sel, v_sel, sel, k_chunk, v_chunk, s, h, Hkv, c_off, h_off,
+                                 Lh, kv_budget, t_last, wave);
+  const int n1 = kv.n1;
   const int n_all = n1 + (t_last + KT) / KT;
-  const uint32_t rb1 = kIdx ? (uint32_t)Hkv * D * 2u : D * 2u;
-  const uint32_t rb2 = (uint32_t)Hkv * D * 2u;
-  const uint32_t end1 = kIdx ? (Lh > 0 ? (uint32_t)(Lh - 1) * rb1 + D * 2u : 0u)
-                             : (uint32_t)B_eff * rb1;
-  const uint32_t end2 = (uint32_t)t_last * rb2 + D * 2u;
-  const int32_t* sidx = sel + prob * kv_budget;
-
-  // LDS slot of 16-byte chunk c of row rr: c ^ kswz(rr) for K, c ^ vswz(rr)
-  // for V. A K read (16 lanes: 16 rows, one chunk) and a V transposing read
-  // (32 lanes: 8 rows, two adjacent chunks) then cover all 64 banks once.
-  constexpr int CPR = D / 8, RPP = 64 / CPR, NP = KT / RPP / NW;
-  auto kswz = [](int rr) { return D == 128 ? (rr & 15) : ((rr >> 1) & 7); };
-  auto vswz = [](int rr) { return D == 128 ? 2 * (rr & 7) : 2 * ((rr >> 1) & 3); };
-  static_assert(NP >= 1 && KT % (RPP * NW) == 0, "tile must split into whole pieces per wave");
-  int prow[NP];
-  uint32_t kcol[NP], vcol[NP];
-#pragma unroll
-  for (int u = 0; u < NP; ++u) {
-    const int rr = (wave * NP + u) * RPP + lane / CPR, sl = lane % CPR;
-    prow[u] = rr;
-    kcol[u] = (uint32_t)(sl ^ kswz(rr)) * 16u;
-    vcol[u] = (uint32_t)(sl ^ vswz(rr)) * 16u;
-  }
-  int nidx[NP];
-  auto fetch_idx = [&](int it) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int key = it * KT + prow[u];
-      nidx[u] = key < B_eff ? sidx[key] : -1;
-    }
-  };
-  if (kIdx && 0 < n1) fetch_idx(0);
-  using lds_ptr = __attribute__((address_space(3))) void*;
-  auto load = [&](int it, bf16* kd, bf16* vd) __attribute__((always_inline)) {
-    const bool ph1 = it < n1;
-    const int kbase = (ph1 ? it : it - n1) * KT;
-    if (kIdx && ph1) {
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k1, end1), rv = make_rsrc(v1, end1);
-#pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        const int row = nidx[u];
-        const bool ok = (unsigned)row < (unsigned)Lh;
-        const uint32_t base = (uint32_t)row * rb1;
-        bf16* kp = kd + (wave * NP + u) * 512;
-        bf16* vp = vd + (wave * NP + u) * 512;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(ok ? base + kcol[u] : end1), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(ok ? base + vcol[u] : end1), 0, 0, 0);
-      }
-      if (it + 1 < n1) fetch_idx(it + 1);
-      return;
-    }
-    const uint32_t rb = ph1 ? rb1 : rb2;
-    const uint32_t skip = (uint32_t)kbase * rb;
-    const uint32_t left = (ph1 ? end1 : end2) - skip;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((ph1 ? k1 : k2) + (int64_t)kbase * (rb / 2), left);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((ph1 ? v1 : v2) + (int64_t)kbase * (rb / 2), left);
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const uint32_t base = (uint32_t)prow[u] * rb;
-      bf16* kp = kd + (wave * NP + u) * 512;
-      bf16* vp = vd + (wave * NP + u) * 512;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)kp, 16, (int)(base + kcol[u]), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)vp, 16, (int)(base + vcol[u]), 0, 0, 0);
-    }
-  };
-  if (0 < n_all) load(0, Ks0, Vs0);
+  using Swz = KVSwizzle<D, true>;
+  if (kIdx && 0 < n1) kv.fetch_idx(0);
+  if (0 < n_all) kv.load(0, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // K operand of (key block kb, d-step ds): row kb*16 + l%16, chunk
-  // ds*4 + l/16 (kb*16 leaves kswz unchanged)
+  // ds*4 + l/16 (kb*16 leaves the swizzle unchanged)
   int koff[NDS];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) koff[ds] = rl * D + (((ds * 4 + g4) ^ kswz(rl)) << 3);
+  for (int ds = 0; ds < NDS; ++ds) koff[ds] = rl * D + (((ds * 4 + g4) ^ Swz::k(rl)) << 3);
   // V^T operand of d-block db: 16-lane group g reads keys g*4 + j/4 (+16 for
   // the second half of the step), columns db*16 + 4 (j%4), j = l%16
   int voff[NDB];
@@ -661,7 +631,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_r16_kernel(
   for (int db = 0; db < NDB; ++db) {
     const int row = g4 * 4 + (rl >> 2);
     const int c = db * 2 + ((rl & 3) >> 1);
-    voff[db] = row * D + ((c ^ vswz(row)) << 3) + 4 * (rl & 1);
+    voff[db] = row * D + ((c ^ Swz::v(row)) << 3) + 4 * (rl & 1);
   }
   const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
 
@@ -669,7 +639,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? 2 : 1)) void attn_r16_kernel(
     constexpr int B = decltype(Bc)::value;
     const bf16* ks = B ? Ks1 : Ks0;
     const bf16* vs = B ? Vs1 : Vs0;
-    if (it + 1 < n_all) load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
+    if (it + 1 < n_all) kv.load(it + 1, B ? Ks0 : Ks1, B ? Vs0 : Vs1);
     const bool ph1 = it < n1;
     const int kbase = (ph1 ? it : it - n1) * KT;
     if (wave_live && (ph1 || kbase <= t_wave_last)) {
