@@ -106,8 +106,11 @@ def test_fused_gather_handles_padding_and_bad_indices():
         assert torch.equal(out, fused)
 
 
-def test_repeat_runs_are_bitwise_identical():
-    w = _case("bf16_d128_g7_maxq")
+@pytest.mark.parametrize("name", ["bf16_d128_g7_maxq", "bf16_four_wave_unsplit"])
+def test_repeat_runs_are_bitwise_identical(name):
+    # key ranges merged afterwards; and sixteen rows per wave
+    print(f"[gpu] repeat runs {name}", flush=True)
+    w = _case(name)
     shape, t = upload(w)
     ws = cpk.alloc_workspace(shape, w.n_q, w.budget)
     outs = []
