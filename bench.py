@@ -86,18 +86,11 @@ def gather_bytes(w) -> float:
 
 
 def attention_kernel_name(w) -> str:
-    """The attention kernel the library launches for this layer: the fp32 VALU kernel, the
-    16-rows-per-wave kernel where 32-row four-wave tiles would be between 129 and 256 (at
-    most one per CU, no key split), else the 32-row kernel (the library's attention plan;
-    this only names the kernel in the roofline entry)."""
-    if w.dtype != "bf16":
-        return "attn_valu_kernel"
-    G = w.num_q_heads // w.num_kv_heads
-    maxc = int(np.max(np.diff(w.cu_chunk)))
-    rows = maxc * G
-    grid4 = (rows + 127) // 128 * w.num_kv_heads * w.num_seqs
-    many = (rows + 255) // 256 * w.num_kv_heads * w.num_seqs >= 512
-    return "attn_r16_kernel" if (not many and 128 < grid4 <= 256) else "attn_mfma_kernel"
+    """The attention kernel the library launches for this layer (quoka_attn_plan)."""
+    import chunked_prefill_kv_amd as cpk
+    shape = cpk.Shape(w.cu_chunk, w.cu_hist, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                      w.dtype, device="cpu")
+    return cpk.ATTN_KERNELS[cpk.attn_plan(shape, w.budget)[0]]
 
 
 def measured_traffic(config: str, kernel: str, source: str):

@@ -22,6 +22,20 @@ LIB_PATH = os.path.join(_PKG, "lib", "libquoka.so")
 
 QUOKA_OK, QUOKA_EINVAL, QUOKA_EUNSUPPORTED, QUOKA_EWORKSPACE, QUOKA_EHIP, QUOKA_ECHECK = range(6)
 QUOKA_F32, QUOKA_BF16 = 0, 1
+# quoka_attn_kernel values and the kernel functions they name
+ATTN_KERNELS = {0: "attn_valu_kernel", 1: "attn_mfma_kernel", 2: "attn_mfma_kernel",
+                3: "attn_mfma_kernel", 4: "attn_r16_kernel"}
+
+
+def attn_plan(shape: Shape, kv_budget: int):
+    """(quoka_attn_kernel value, key ranges) of the attention launched for this shape."""
+    lib = load_library()
+    k, n = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.quoka_attn_plan(ctypes.byref(shape.c), kv_budget, ctypes.byref(k), ctypes.byref(n)),
+           "quoka_attn_plan")
+    return int(k.value), int(n.value)
+
+
 MAX_Q_BUDGET = 128
 # quoka_variant: QUOKA and the baseline selections the pages compare it with
 VARIANTS = {"quoka": 0, "dot": 1, "mean_queries": 2, "mean_query": 3, "per_head": 4,
@@ -29,7 +43,7 @@ VARIANTS = {"quoka": 0, "dot": 1, "mean_queries": 2, "mean_query": 3, "per_head"
 
 SYMBOLS = ("quoka_workspace_bytes", "quoka_select", "quoka_select_profiled",
            "quoka_select_variant", "quoka_gather", "quoka_check_selection",
-           "quoka_attn_workspace_bytes", "quoka_chunk_attn",
+           "quoka_attn_workspace_bytes", "quoka_attn_plan", "quoka_chunk_attn",
            "quoka_chunk_attn_gather", "quoka_prefill_chunk", "quoka_prefill_chunk_static",
            "quoka_prompt_workspace_bytes",
            "quoka_prefill_prompt", "quoka_strerror", "quoka_last_error")
@@ -89,6 +103,7 @@ def load_library(path: str = LIB_PATH):
     lib.quoka_gather.argtypes = [sp, vp, vp, vp, i32, vp, vp, vp]
     lib.quoka_check_selection.argtypes = [sp, vp, i32, vp]
     lib.quoka_attn_workspace_bytes.argtypes = [sp, i32, P(sz)]
+    lib.quoka_attn_plan.argtypes = [sp, i32, P(i32), P(i32)]
     lib.quoka_chunk_attn.argtypes = [sp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.quoka_chunk_attn_gather.argtypes = [sp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp,
                                             vp, sz, vp]

@@ -477,6 +477,20 @@ quoka_status quoka_check_selection(const quoka_shape* shape, const int32_t* sel_
   return debug_run(p, &it, 1, stream);
 }
 
+quoka_status quoka_attn_plan(const quoka_shape* shape, int32_t kv_budget, int32_t* kernel,
+                             int32_t* key_ranges) {
+  g_err[0] = 0;
+  if (!kernel || !key_ranges) return fail(QUOKA_EINVAL, "kernel or key_ranges is null");
+  Problem p;
+  quoka_status rc = make_problem(shape, 1, kv_budget, &p);
+  if (rc != QUOKA_OK) return rc;
+  int k = 0, n = 1;
+  attn_describe(p, &k, &n);
+  *kernel = k;
+  *key_ranges = n;
+  return QUOKA_OK;
+}
+
 quoka_status quoka_attn_workspace_bytes(const quoka_shape* shape, int32_t kv_budget,
                                         size_t* bytes) {
   g_err[0] = 0;

@@ -824,6 +824,19 @@ AttnPlan attn_plan(const Problem& p) {
 
 }  // namespace
 
+void attn_describe(const Problem& p, int* kernel, int* key_ranges) {
+  if (p.dtype != QUOKA_BF16) {
+    *kernel = QUOKA_ATTN_VALU;
+    *key_ranges = 1;
+    return;
+  }
+  const AttnPlan a = attn_plan(p);
+  *kernel = a.r16 ? QUOKA_ATTN_ROWS16
+          : a.nw == 4 ? QUOKA_ATTN_ROWS32_4W
+          : a.pair ? QUOKA_ATTN_ROWS32_8W_PAIRED : QUOKA_ATTN_ROWS32_8W;
+  *key_ranges = a.nsplit;
+}
+
 size_t attn_workspace_bytes(const Problem& p) {
   if (p.dtype != QUOKA_BF16 || p.maxC == 0) return 0;
   const AttnPlan a = attn_plan(p);

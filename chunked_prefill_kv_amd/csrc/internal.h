@@ -141,6 +141,8 @@ hipError_t launch_gather(const Problem& p, const void* k_hist, const void* v_his
 // to attn_ws, attn_workspace_bytes(p) bytes (0: no split, attn_ws unused),
 // and are merged by a second launch.
 size_t attn_workspace_bytes(const Problem& p);
+// The attention kernel (quoka_attn_kernel) and key ranges launch_attention uses.
+void attn_describe(const Problem& p, int* kernel, int* key_ranges);
 hipError_t launch_attention(const Problem& p, const void* q, const void* k_sel,
                             const void* v_sel, const int32_t* sel, const void* k_chunk,
                             const void* v_chunk, float scale, void* out, void* attn_ws,

@@ -230,6 +230,20 @@ quoka_status quoka_check_selection(const quoka_shape* shape, const int32_t* sel_
 quoka_status quoka_attn_workspace_bytes(const quoka_shape* shape,
                                         int32_t kv_budget, size_t* bytes);
 
+/* Which attention kernel quoka_chunk_attn(_gather) and quoka_prefill_chunk
+ * launch for this shape, for measurement and tests (host only, nothing
+ * runs): *kernel one of the quoka_attn_kernel values, *key_ranges the number
+ * of key ranges each query tile's keys are split into (1: no split). */
+typedef enum quoka_attn_kernel {
+  QUOKA_ATTN_VALU = 0,            /* fp32: one token per lane */
+  QUOKA_ATTN_ROWS32_4W = 1,       /* bf16 MFMA, 32 rows per wave, four waves */
+  QUOKA_ATTN_ROWS32_8W = 2,       /* eight waves on 256 contiguous rows */
+  QUOKA_ATTN_ROWS32_8W_PAIRED = 3,/* eight waves on a heavy and a light 128-row tile */
+  QUOKA_ATTN_ROWS16 = 4           /* 16 rows per wave, eight waves per 128-row tile */
+} quoka_attn_kernel;
+quoka_status quoka_attn_plan(const quoka_shape* shape, int32_t kv_budget,
+                             int32_t* kernel, int32_t* key_ranges);
+
 /* Chunk attention: step 4 ("Background > Chunked prefill"; "QUOKA Method":
  * the reduced KV set goes to a dense attention kernel). Query row (t, j) of
  * sequence s attends to the first B_eff rows of k_sel / v_sel[s, j / G] and to

@@ -202,3 +202,27 @@ def test_peak_probe_library_exports_its_probes(lib):
     names = set(re.findall(r"\bT (quoka_peaks_\w+)", out))
     assert names == {"quoka_peaks_mfma", "quoka_peaks_read", "quoka_peaks_clock",
                      "quoka_peaks_device"}
+
+
+def test_attention_plan_of_the_layer_shapes(lib):
+    """quoka_attn_plan (host only): the kernel and key ranges each layer shape's attention
+    takes, as the benchmark names them in its roofline entry."""
+    ragged_hist = [0]
+    for k in (4, 8, 16, 24, 32, 48, 64, 96):
+        ragged_hist.append(ragged_hist[-1] + k * 1024)
+    cases = {
+        # name: (cu_chunk, cu_hist, H_q, H_kv, d, dtype, B) -> (kernel, key ranges)
+        "tiny": (([0, 128], [0, 1024], 1, 1, 64, "fp32", 128), (0, 1)),
+        "llama8b": (([0, 2048], [0, 32768], 32, 8, 128, "bf16", 2048), (3, 1)),
+        "long": (([0, 4096], [0, 131072], 32, 8, 128, "bf16", 4096), (2, 1)),
+        "narrow": (([0, 1024], [0, 65536], 28, 4, 128, "bf16", 1024), (4, 1)),
+        "ragged": (([512 * i for i in range(9)], ragged_hist, 32, 8, 128, "bf16", 1024), (3, 1)),
+        "decode": ((list(range(9)), [16384 * i for i in range(9)], 32, 8, 128, "bf16", 2048),
+                   (1, 4)),
+    }
+    for name, ((cc, ch, hq, hkv, d, dt, b), want) in cases.items():
+        shape = cpk.Shape(cc, ch, hq, hkv, d, dt, device="cpu")
+        assert cpk.attn_plan(shape, b) == want, name
+    k = ctypes.c_int32(0)
+    shape = _host_shape([0, 100], [0, 1000])
+    assert lib.quoka_attn_plan(ctypes.byref(shape.c), 64, ctypes.byref(k), None) == cpk.QUOKA_EINVAL
